@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""SegPagedAttention prefill benchmark on one MI355X.
+
+One step is one pass of the whole SegPaged prefill path over the 32K-context,
+Mistral-7B-shaped layer (32 q heads, 8 kv heads, D=128, 16 reused 2K segments
++ a 512-token query segment; kv head 0 global, 1..7 local with a 1024 window):
+  1. segkv_build_pages     per-head page tables, head-aware move list, plan
+  2. rope_relocate         head-aware moves: cached K rotated + V gathered
+  3. segpaged_attn_prefill attention over the visible pages (+ split merge)
+  4. token_importance_topk importance over the last 64 rows, top 25% of keys
+`value` is the visible-pair attention FLOPs (4 * D * sum of visible keys over
+every (query head, row)) per second of whole-step time. The line also carries
+the attention call's own rate against the bf16 MFMA peak (roofline), the full
+relocation's HBM bandwidth, the sparse FFN of the 8K selection workload, and
+the fp64 oracle timed on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def visible_pairs_per_row(w):
+    """Per query row: visible keys summed over query heads (closed form per class)."""
+    import numpy as np
+    G = w.num_q_heads // w.num_kv_heads
+    out = np.zeros(w.total_q_rows, dtype=np.int64)
+    for r in range(w.num_requests):
+        sq = w.query_segment(r)
+        bq, lq = int(w.seg_start[sq]), int(w.seg_len[sq])
+        i = np.arange(bq, bq + lq, dtype=np.int64)
+        for h in range(w.num_kv_heads):
+            k = r * w.num_kv_heads + h
+            c = int(w.head_class[k])
+            if c in (0, 3):
+                n = i + 1
+            elif c == 1:
+                n = i - np.maximum(0, np.minimum(bq, i - int(w.window[k]) + 1)) + 1
+            else:
+                segs = [int(s) for s in w.retr_seg[2 * k:2 * k + 2]]
+                n = (i - bq + 1) + sum(int(w.seg_len[s]) for s in segs)
+            out[int(w.cu_q[r]):int(w.cu_q[r + 1])] += G * n
+    return out
+
+
+def profile_traffic(kernel_tag, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if line.startswith("|") and ":" not in line.split("|")[1]:
+            continue
+        if line.startswith("- ") and "=" in line:
+            k, v = line[2:].split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != src_hash or "hbm_bytes_per_launch" not in vals:
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
+def source_hash(names):
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(ROOT, "head_aware_paged_amd", "csrc", n), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(w, pairs_per_row, n_rows):
+    """The fp64 oracle on a bounded sample of the same workload (first n_rows query rows)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    rows = list(range(n_rows))
+    t0 = time.perf_counter()
+    oracle.attention(w, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.head_dim * float(sum(pairs_per_row[:n_rows]))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 oracle attention on query rows 0..{n_rows - 1} of {w.total_q_rows} (all {w.num_q_heads} "
+                      f"q heads) of {w.name}: {flops / 1e9:.2f} GFLOP visible-pair in {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-rows", type=int, default=128)
+    ap.add_argument("--skip-extras", action="store_true", help="only the timed steps (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(a kv-head-sharded design is described in the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from head_aware_paged_amd.session import SegPagedLayer, SparseFFN
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+
+    def bf16(u):
+        return torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+
+    log("generating mistral7b_32k workload")
+    w = workloads.mistral_32k(fill_reused_work=False)
+    per_row = visible_pairs_per_row(w)
+    pairs = int(per_row.sum())
+    flops = 4.0 * w.head_dim * pairs
+    log(f"visible pairs {pairs} ({flops / 1e9:.2f} GFLOP per attention call)")
+    layer = SegPagedLayer(w.num_q_heads, w.num_kv_heads, w.head_dim, w.seg_indptr, w.seg_start, w.seg_len,
+                          w.head_class, w.window, w.retr_seg, device=dev)
+    q, k_work, v_work = bf16(w.q), bf16(w.k_work), bf16(w.v_work)
+    k_cache, v_cache = bf16(w.k_cache), bf16(w.v_cache)
+    spi, sp = i32(w.seg_page_indptr), i32(w.seg_pages)
+    cpi, cp, sos = i32(w.cache_page_indptr), i32(w.cache_pages), i32(w.seg_orig_start)
+    T, Hq, D = w.total_q_rows, w.num_q_heads, w.head_dim
+    out = torch.empty(T, Hq, D, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(T, Hq, dtype=torch.float32, device=dev)
+    Lk = w.context_len(0)
+    n_last, ksel = 64, [Lk // 4]
+    imp = torch.empty(Lk, dtype=torch.float32, device=dev)
+    idx = torch.empty(ksel[0], dtype=torch.int32, device=dev)
+
+    ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+          for n in ("pages", "reloc", "attn", "imp", "end")}
+
+    def step(i=None):
+        e = (lambda n: ev[n][i].record()) if i is not None else (lambda n: None)
+        e("pages")
+        layer.build_pages(spi, sp, cpi, cp, sos)
+        e("reloc")
+        layer.relocate(k_cache, k_work, v_cache, v_work, w.rope_theta)
+        e("attn")
+        layer.attention(q, k_work, v_work, out=out, lse=lse)
+        e("imp")
+        layer.importance_topk(q, k_work, lse, n_last, ksel, importance=imp, topk_idx=idx)
+        e("end")
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+
+    def avg_ms(a, b):
+        return sum(ev[a][i].elapsed_time(ev[b][i]) for i in range(args.steps)) / args.steps
+
+    t_pages, t_reloc = avg_ms("pages", "reloc"), avg_ms("reloc", "attn")
+    t_attn, t_imp = avg_ms("attn", "imp"), avg_ms("imp", "end")
+    attn_tflops = flops / (t_attn * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms: pages {t_pages * 1e3:.1f} us, relocate {t_reloc * 1e3:.1f} us, "
+        f"attention {t_attn * 1e3:.1f} us ({attn_tflops:.1f} TFLOP/s), importance+topk {t_imp * 1e3:.1f} us")
+    ha_bytes = 2.0 * layer.num_moves * 16 * D * 2 * 2  # K+V pages, read + write
+
+    result = {
+        "metric": "visible-pair attention TFLOP/s + % bf16 MFMA peak at 32K; relocate GB/s",
+        "value": flops * args.steps / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "mistral7b_32k", "context": Lk, "query_rows": T, "q_heads": Hq,
+                   "kv_heads": w.num_kv_heads, "head_dim": D, "page_size": 16,
+                   "head_classes": "kv0 global, kv1-7 local(1024)", "visible_pairs": pairs,
+                   "step": "build_pages + rope_relocate(head-aware moves, K+V) + segpaged_attn_prefill + "
+                           "token_importance_topk(last 64 rows, k=25%)"},
+        "breakdown_us": {"build_pages": t_pages * 1e3, "rope_relocate_head_aware": t_reloc * 1e3,
+                         "segpaged_attn_prefill": t_attn * 1e3, "token_importance_topk": t_imp * 1e3},
+        "attention": {"tflops": attn_tflops, "pct_bf16_peak": 100.0 * attn_tflops / PEAK_BF16_TFLOPS},
+        "relocate_head_aware": {"moves": layer.num_moves, "GB/s": ha_bytes / (t_reloc * 1e-3) / 1e9},
+    }
+    traffic = profile_traffic("attn_main_mistral7b_32k", source_hash(["attention.hip", "plan.h", "common.h"]))
+    result["roofline"] = {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                          "kernel": "segpaged_attn_prefill (attn_main_kernel + attn_combine_kernel)",
+                          "algorithmic": f"{flops / 1e9:.3f} GFLOP per launch = 4*D*visible pairs"}
+
+    if not args.skip_extras:
+        # full relocation bandwidth (every reused page, K+V), three rotating buffer sets > 2x Infinity Cache
+        from head_aware_paged_amd import rope_relocate
+        Hkv = w.num_kv_heads
+        src, dst, dl = [], [], []
+        for s in w.segments_of(0)[:-1]:
+            for h in range(Hkv):
+                a, b = w.cache_page_indptr[s * Hkv + h], w.cache_page_indptr[s * Hkv + h + 1]
+                c, d = w.seg_page_indptr[s * Hkv + h], w.seg_page_indptr[s * Hkv + h + 1]
+                src.extend(w.cache_pages[a:b]); dst.extend(w.seg_pages[c:d])
+                dl.extend([int(w.seg_start[s] - w.seg_orig_start[s])] * (b - a))
+        src_t, dst_t, dl_t = i32(src), i32(dst), i32(dl)
+        n_mv = len(src)
+        sets = [(k_cache, v_cache, k_work, v_work)] + [
+            (k_cache.clone(), v_cache.clone(), k_work.clone(), v_work.clone()) for _ in range(2)]
+        reps = 30
+        for kv in (True, False):
+            tot = 0.0
+            for rep in range(reps + 3):
+                kc, vc, kw, vw = sets[rep % 3]
+                a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record()
+                rope_relocate(kc, kw, vc if kv else None, vw if kv else None, src_t, dst_t, dl_t, n_mv, 16, D,
+                              w.rope_theta)
+                a1.record()
+                torch.cuda.synchronize()
+                if rep >= 3:
+                    tot += a0.elapsed_time(a1)
+            t = tot / reps
+            nbytes = 2.0 * n_mv * 16 * D * 2 * (2 if kv else 1)
+            result["relocate_full_kv" if kv else "relocate_full_k"] = {
+                "moves": n_mv, "bytes": nbytes, "us": t * 1e3, "GB/s": nbytes / (t * 1e-3) / 1e9,
+                "pct_hbm_peak": 100.0 * nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+        # plain device copy of 256 MiB, for calibration
+        xa = torch.empty(128 << 20, dtype=torch.bfloat16, device=dev)
+        xb = torch.empty_like(xa)
+        for _ in range(3):
+            xb.copy_(xa)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(10):
+            xb.copy_(xa)
+        a1.record()
+        torch.cuda.synchronize()
+        result["copy_256MiB_GB/s"] = 2.0 * xa.numel() * 2 * 10 / (a0.elapsed_time(a1) * 1e-3) / 1e9
+        del xa, xb, sets
+        log(f"relocate full K+V {result['relocate_full_kv']['GB/s']:.0f} GB/s, "
+            f"K only {result['relocate_full_k']['GB/s']:.0f} GB/s, copy {result['copy_256MiB_GB/s']:.0f} GB/s")
+
+        # sparse SwiGLU FFN of the 8K selection workload (k = 2048 rows, 4096 -> 14336)
+        log("generating sparse_ffn_8k FFN inputs")
+        w5 = workloads.sparse_ffn_8k()
+        hid = bf16(w5.hidden)
+        ffn = SparseFFN(bf16(w5.w_gate), bf16(w5.w_up), bf16(w5.w_down), k_max=w5.topk)
+        sel = i32(np.arange(0, 8192, 4))
+        for _ in range(2):
+            ffn(hid, sel, w5.topk)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(5):
+            ffn(hid, sel, w5.topk)
+        a1.record()
+        torch.cuda.synchronize()
+        t = a0.elapsed_time(a1) / 5
+        ffn_flops = 6.0 * w5.topk * 4096 * 14336
+        result["sparse_ffn_8k"] = {"rows": w5.topk, "us": t * 1e3, "tflops": ffn_flops / (t * 1e-3) / 1e12,
+                                   "pct_bf16_peak": 100.0 * ffn_flops / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        log(f"sparse FFN {result['sparse_ffn_8k']['tflops']:.1f} TFLOP/s")
+        del hid, ffn
+
+        log(f"cpu baseline: oracle on {args.cpu_rows} rows")
+        result["cpu_baseline"] = cpu_baseline(w, per_row, args.cpu_rows)
+        log(f"cpu baseline {result['cpu_baseline']['value'] * 1e3:.2f} GFLOP/s")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,382 @@
+// SELECTVISIBLESTATE: per-(request, kv head) page tables, the head-aware
+// relocation move list, the attention work plan, and the visible-span export.
+//
+// RedKnot README ("About": per-head page table + segmented KV store, per-class
+// visible windows); paooo.com "如何使用RedKnot" (SELECTVISIBLESTATE chooses
+// the local-head KV to reuse and the global-head ranges to recompute). All of
+// it is integer work on small metadata; it runs on the device so that nothing
+// has to be copied from the host between the calls of one layer.
+#include "common.h"
+
+namespace segkv {
+namespace {
+
+constexpr int kScanThreads = 1024;
+
+// Exclusive prefix sum over n values produced by value(i), processed in
+// chunks of the block size; write(i, prefix) receives each result and the
+// total is returned (uniform across the block). Block-wide; all threads call it.
+template <class F, class W>
+__device__ int block_exclusive_scan(int n, F value, W write, int* s) {
+  int carry = 0;
+  const int tid = threadIdx.x;
+  for (int base = 0; base < n; base += kScanThreads) {
+    const int i = base + tid;
+    const int v = i < n ? value(i) : 0;
+    s[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kScanThreads; off <<= 1) {
+      const int t = tid >= off ? s[tid - off] : 0;
+      __syncthreads();
+      s[tid] += t;
+      __syncthreads();
+    }
+    if (i < n) write(i, carry + s[tid] - v);
+    const int tot = s[kScanThreads - 1];
+    __syncthreads();
+    carry += tot;
+  }
+  return carry;
+}
+
+struct PagesArgs {
+  segkv_meta m;
+  const int32_t* cu_q;
+  const int32_t* seg_page_indptr;
+  const int32_t* seg_pages;
+  int32_t* page_indptr;
+  int32_t* page_ids;
+  int32_t* page_pos;
+  const int32_t* cache_page_indptr;
+  const int32_t* cache_pages;
+  const int32_t* seg_orig_start;
+  int32_t* move_src;
+  int32_t* move_dst;
+  int32_t* move_delta;
+  char* plan;
+  int R, Hkv, G;
+  int chunk_tiles;
+  PlanLayout L;
+};
+
+// Table sizes -> page_indptr and move counts -> move offsets (block-wide).
+__device__ void table_offsets(const PagesArgs& a, int* s) {
+  const int n = a.R * a.Hkv;
+  int32_t* move_off = reinterpret_cast<int32_t*>(a.plan + a.L.move_off_off);
+  const int tot = block_exclusive_scan(
+      n,
+      [&](int k) {
+        const HeadView v = head_view_dev(a.m, a.Hkv, k / a.Hkv, k % a.Hkv);
+        return runs_count(head_page_runs(v));
+      },
+      [&](int k, int p) { a.page_indptr[k] = p; }, s);
+  const int mtot = block_exclusive_scan(
+      n,
+      [&](int k) {
+        const HeadView v = head_view_dev(a.m, a.Hkv, k / a.Hkv, k % a.Hkv);
+        return runs_rank(head_page_runs(v), v.bq / kPage);
+      },
+      [&](int k, int p) { move_off[k] = p; }, s);
+  if (threadIdx.x == 0) {
+    a.page_indptr[n] = tot;
+    move_off[n] = mtot;
+  }
+  __syncthreads();
+}
+
+// Grid (pair, entry block): fill 256 table entries of pair (r, h) and their moves.
+__global__ __launch_bounds__(256) void table_fill_kernel(PagesArgs a) {
+  const int k = blockIdx.x;
+  const int r = k / a.Hkv, h = k % a.Hkv;
+  const int e = blockIdx.y * blockDim.x + threadIdx.x;
+  const HeadView v = head_view_dev(a.m, a.Hkv, r, h);
+  const PageRuns pr = head_page_runs(v);
+  if (e >= runs_count(pr)) return;
+  const int base = a.page_indptr[k];
+  const int32_t* move_off = reinterpret_cast<const int32_t*>(a.plan + a.L.move_off_off);
+  const int s0 = a.m.seg_indptr[r], s1 = a.m.seg_indptr[r + 1];
+  const int p = runs_page(pr, e);
+  const int tok = p * kPage;
+  // segment holding this page: last segment with start <= tok
+  int lo = s0, hi = s1 - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.m.seg_start[mid] <= tok) lo = mid; else hi = mid - 1;
+  }
+  const int s = lo;
+  const int qpage = (tok - a.m.seg_start[s]) / kPage;
+  const int phys = a.seg_pages[a.seg_page_indptr[s * a.Hkv + h] + qpage];
+  a.page_ids[base + e] = phys;
+  a.page_pos[base + e] = tok;
+  if (a.move_src != nullptr && s != s1 - 1) {
+    // reused pages precede the query segment's pages in the ascending table
+    const int mi = move_off[k] + e;
+    a.move_src[mi] = a.cache_pages[a.cache_page_indptr[s * a.Hkv + h] + qpage];
+    a.move_dst[mi] = phys;
+    a.move_delta[mi] = a.m.seg_start[s] - a.seg_orig_start[s];
+  }
+}
+
+// One block: table offsets, then the m-tile descriptors, partial slots, split
+// list and the item list ordered from the largest item to the smallest
+// (longest-first dispatch).
+__global__ __launch_bounds__(kScanThreads) void plan_kernel(PagesArgs a) {
+  __shared__ int s[kScanThreads];
+  __shared__ int bins[1024];
+  const int tid = threadIdx.x;
+  table_offsets(a, s);
+  PlanHeader* hdr = reinterpret_cast<PlanHeader*>(a.plan);
+  int32_t* req_off = reinterpret_cast<int32_t*>(a.plan + a.L.req_mt_off);
+  MTile* mt = reinterpret_cast<MTile*>(a.plan + a.L.mtiles_off);
+  Item* items = reinterpret_cast<Item*>(a.plan + a.L.items_off);
+  int32_t* split = reinterpret_cast<int32_t*>(a.plan + a.L.split_off);
+  const int MP = mtile_positions(a.G);
+  const int S = a.chunk_tiles;
+
+  // m-tiles per request (Hkv heads x ceil(Lq / MP) position blocks)
+  const int n_mt = block_exclusive_scan(
+      a.R,
+      [&](int r) {
+        const int sq = a.m.seg_indptr[r + 1] - 1;
+        return a.Hkv * cdiv(a.m.seg_len[sq], MP);
+      },
+      [&](int r, int p) { req_off[r] = p; }, s);
+  if (tid == 0) req_off[a.R] = n_mt;
+  __syncthreads();
+
+  // descriptors, one m-tile per thread
+  for (int i = tid; i < n_mt; i += blockDim.x) {
+    int lo = 0, hi = a.R - 1;  // request: last r with req_off[r] <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (req_off[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const int r = lo;
+    const int nj = (req_off[r + 1] - req_off[r]) / a.Hkv;
+    const int h = (i - req_off[r]) / nj, j = (i - req_off[r]) % nj;
+    const HeadView v = head_view_dev(a.m, a.Hkv, r, h);
+    const PageRuns pr = head_page_runs(v);
+    const int base = a.page_indptr[r * a.Hkv + h];
+    const int t0 = j * MP;
+    const int i_lo = v.bq + t0, i_hi = v.bq + imin(v.Lq, t0 + MP) - 1;
+    int e0, e1;
+    mtile_entries(v, pr, i_lo, i_hi, &e0, &e1);
+    MTile d;
+    d.r = r;
+    d.h = h;
+    d.q_row0 = a.cu_q[r] + t0;
+    d.n_pos = imin(v.Lq, t0 + MP) - t0;
+    d.pos0 = i_lo;
+    d.cls = v.cls;
+    d.W = v.W;
+    d.bq = v.bq;
+    d.e_begin = base + e0;
+    d.e_end = base + e1;
+    d.n_tiles = cdiv(e1 - e0, kTilePages);
+    d.n_chunks = num_chunks(d.n_tiles, S);
+    d.partial_base = -1;
+    d.pad[0] = d.pad[1] = d.pad[2] = 0;
+    mt[i] = d;
+  }
+  __syncthreads();
+
+  const int n_partials = block_exclusive_scan(
+      n_mt, [&](int i) { return mt[i].n_chunks > 1 ? mt[i].n_chunks : 0; },
+      [&](int i, int p) {
+        if (mt[i].n_chunks > 1) mt[i].partial_base = p;
+      },
+      s);
+  const int n_split = block_exclusive_scan(
+      n_mt, [&](int i) { return mt[i].n_chunks > 1 ? 1 : 0; },
+      [&](int i, int p) {
+        if (mt[i].n_chunks > 1) split[p] = i;
+      },
+      s);
+
+  // items bucketed by size (1024 size classes, largest first)
+  for (int b = tid; b < 1024; b += blockDim.x) bins[b] = 0;
+  __syncthreads();
+  // size classes: 1024 * (size - 1) / S fits in 32 bits because S <= 2^18 (contexts <= 2^24 tokens)
+  auto size_bin = [&](int sz) { return 1023 - ((sz - 1) * 1024) / S; };
+  for (int i = tid; i < n_mt; i += blockDim.x) {
+    const int nt = mt[i].n_tiles, nc = mt[i].n_chunks;
+    for (int c = 0; c < nc; ++c) {
+      const int sz = chunk_tile_lo(nt, nc, c + 1) - chunk_tile_lo(nt, nc, c);
+      atomicAdd(&bins[size_bin(sz)], 1);
+    }
+  }
+  __syncthreads();
+  __shared__ int n_items_s;
+  {  // bin counts -> start cursors (largest size class first), block-parallel
+    const int c = bins[tid];
+    s[tid] = c;
+    __syncthreads();
+    for (int off = 1; off < kScanThreads; off <<= 1) {
+      const int t = tid >= off ? s[tid - off] : 0;
+      __syncthreads();
+      s[tid] += t;
+      __syncthreads();
+    }
+    bins[tid] = s[tid] - c;
+    if (tid == kScanThreads - 1) n_items_s = s[tid];
+  }
+  __syncthreads();
+  const int n_items = n_items_s;
+  for (int i = tid; i < n_mt; i += blockDim.x) {
+    const int nt = mt[i].n_tiles, nc = mt[i].n_chunks;
+    for (int c = 0; c < nc; ++c) {
+      const int sz = chunk_tile_lo(nt, nc, c + 1) - chunk_tile_lo(nt, nc, c);
+      const int slot = atomicAdd(&bins[size_bin(sz)], 1);
+      items[slot] = Item{i, c};
+    }
+  }
+  if (tid == 0) {
+    PlanHeader h;
+    h.n_mtiles = n_mt;
+    h.n_items = n_items;
+    h.n_split = n_split;
+    h.chunk_tiles = S;
+    h.n_partials = n_partials;
+    h.total_q_rows = a.cu_q[a.R];
+    h.max_tiles = 0;
+    h.reserved = 0;
+    for (int q = 0; q < 8; ++q) h.pad[q] = 0;
+    *hdr = h;
+  }
+}
+
+// One thread per (query row, kv head).
+__global__ __launch_bounds__(256) void spans_kernel(segkv_meta m, const int32_t* cu_q, int R, int Hkv,
+                                                    int total_rows, int32_t* spans) {
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total_rows * Hkv) return;
+  const int row = gid / Hkv, h = gid % Hkv;
+  int lo = 0, hi = R - 1;  // request: last r with cu_q[r] <= row
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  const int r = lo;
+  const HeadView v = head_view_dev(m, Hkv, r, h);
+  const int i = v.bq + (row - cu_q[r]);
+  int a[3], b[3], n = 0;
+  if (v.cls == kClassLocal) {
+    a[0] = local_lo(i, v.bq, v.W);
+    b[0] = i + 1;
+    n = 1;
+  } else if (v.cls == kClassRetrieval) {
+    int x[3] = {v.rlo[0], v.rlo[1], v.bq}, y[3] = {v.rhi[0], v.rhi[1], i + 1};
+    for (int p = 1; p < 3; ++p)
+      for (int q = p; q > 0 && x[q] < x[q - 1]; --q) {
+        int t = x[q]; x[q] = x[q - 1]; x[q - 1] = t;
+        t = y[q]; y[q] = y[q - 1]; y[q - 1] = t;
+      }
+    for (int p = 0; p < 3; ++p) {
+      if (n > 0 && x[p] <= b[n - 1]) {
+        b[n - 1] = imax(b[n - 1], y[p]);
+      } else {
+        a[n] = x[p];
+        b[n] = y[p];
+        ++n;
+      }
+    }
+  } else {
+    a[0] = 0;
+    b[0] = i + 1;
+    n = 1;
+  }
+  int32_t* o = spans + (size_t)gid * 6;
+  for (int p = 0; p < 3; ++p) {
+    o[2 * p] = p < n ? a[p] : -1;
+    o[2 * p + 1] = p < n ? b[p] : -1;
+  }
+}
+
+}  // namespace
+}  // namespace segkv
+
+using namespace segkv;
+
+extern "C" int32_t segkv_build_pages(const segkv_dims* dims, const segkv_meta* meta_host,
+                                     const segkv_meta* meta_dev, const int32_t* cu_q_dev,
+                                     const int32_t* seg_page_indptr_dev, const int32_t* seg_pages_dev,
+                                     int32_t* page_indptr_dev, int32_t* page_ids_dev, int32_t* page_pos_dev,
+                                     int64_t table_capacity, const int32_t* cache_page_indptr_dev,
+                                     const int32_t* cache_pages_dev, const int32_t* seg_orig_start_dev,
+                                     int32_t* move_src_dev, int32_t* move_dst_dev, int32_t* move_delta_dev,
+                                     int64_t move_capacity, void* plan_dev, size_t plan_bytes, void* stream) {
+  clear_error();
+  HostPlan hp;
+  int32_t st = compute_host_plan(dims, meta_host, &hp);
+  if (st != SEGKV_OK) return st;
+  if (meta_dev == nullptr || !meta_dev->seg_indptr || !meta_dev->seg_start || !meta_dev->seg_len ||
+      !meta_dev->head_class || !meta_dev->window || !meta_dev->retr_seg)
+    return fail(SEGKV_ERR_INVALID_ARG, "device metadata pointer is NULL");
+  if (!cu_q_dev || !seg_page_indptr_dev || !seg_pages_dev || !page_indptr_dev || !page_ids_dev ||
+      !page_pos_dev || !plan_dev)
+    return fail(SEGKV_ERR_INVALID_ARG, "a required device pointer is NULL");
+  if (table_capacity < hp.table_entries)
+    return fail(SEGKV_ERR_CAPACITY, "table capacity " + std::to_string(table_capacity) + " < " +
+                                         std::to_string(hp.table_entries));
+  const bool moves = move_src_dev != nullptr;
+  if (moves) {
+    if (!move_dst_dev || !move_delta_dev || !cache_page_indptr_dev || !cache_pages_dev || !seg_orig_start_dev)
+      return fail(SEGKV_ERR_INVALID_ARG, "move list requested but a move/cache pointer is NULL");
+    if (move_capacity < hp.move_entries)
+      return fail(SEGKV_ERR_CAPACITY, "move capacity " + std::to_string(move_capacity) + " < " +
+                                           std::to_string(hp.move_entries));
+  }
+  if (plan_bytes < hp.plan_bytes)
+    return fail(SEGKV_ERR_WORKSPACE, "plan buffer " + std::to_string(plan_bytes) + " < " +
+                                         std::to_string(hp.plan_bytes));
+  if (!aligned16(plan_dev)) return fail(SEGKV_ERR_ALIGNMENT, "plan buffer must be 16-byte aligned");
+
+  PagesArgs a;
+  a.m = *meta_dev;
+  a.cu_q = cu_q_dev;
+  a.seg_page_indptr = seg_page_indptr_dev;
+  a.seg_pages = seg_pages_dev;
+  a.page_indptr = page_indptr_dev;
+  a.page_ids = page_ids_dev;
+  a.page_pos = page_pos_dev;
+  a.cache_page_indptr = cache_page_indptr_dev;
+  a.cache_pages = cache_pages_dev;
+  a.seg_orig_start = seg_orig_start_dev;
+  a.move_src = moves ? move_src_dev : nullptr;
+  a.move_dst = move_dst_dev;
+  a.move_delta = move_delta_dev;
+  a.plan = static_cast<char*>(plan_dev);
+  a.R = dims->num_requests;
+  a.Hkv = dims->num_kv_heads;
+  a.G = dims->num_q_heads / dims->num_kv_heads;
+  a.chunk_tiles = hp.chunk_tiles;
+  a.L = plan_layout(a.R * a.Hkv, a.R, hp.n_mtiles, hp.n_items, hp.n_split);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  plan_kernel<<<1, kScanThreads, 0, s>>>(a);
+  SEGKV_LAUNCH_CHECK();
+  int max_pages = 1;
+  for (int r = 0; r < a.R; ++r) {
+    const int sq = meta_host->seg_indptr[r + 1] - 1;
+    max_pages = imax(max_pages, cdiv(meta_host->seg_start[sq] + meta_host->seg_len[sq], kPage));
+  }
+  table_fill_kernel<<<dim3(a.R * a.Hkv, cdiv(max_pages, 256)), 256, 0, s>>>(a);
+  SEGKV_LAUNCH_CHECK();
+  return SEGKV_OK;
+}
+
+extern "C" int32_t segkv_visible_spans(const segkv_dims* dims, const segkv_meta* meta_host,
+                                       const segkv_meta* meta_dev, const int32_t* cu_q_dev, int32_t* spans_dev,
+                                       void* stream) {
+  clear_error();
+  HostPlan hp;
+  int32_t st = compute_host_plan(dims, meta_host, &hp);
+  if (st != SEGKV_OK) return st;
+  if (meta_dev == nullptr || !meta_dev->seg_indptr || !cu_q_dev || !spans_dev)
+    return fail(SEGKV_ERR_INVALID_ARG, "a required device pointer is NULL");
+  const int n = (int)hp.total_q_rows * dims->num_kv_heads;
+  if (n == 0) return SEGKV_OK;
+  spans_kernel<<<cdiv(n, 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      *meta_dev, cu_q_dev, dims->num_requests, dims->num_kv_heads, (int)hp.total_q_rows, spans_dev);
+  SEGKV_LAUNCH_CHECK();
+  return SEGKV_OK;
+}

@@ -1,0 +1,176 @@
+// Shared host/device planning arithmetic for the SegPaged prefill path.
+//
+// Everything here is integer bookkeeping that both the host (sizing, grid
+// shapes) and the device (table fill, attention plan) evaluate; compiling the
+// same functions for both sides keeps them in exact agreement.
+//
+// Visible sets (RedKnot README, "About": each (layer, kv_head) is global /
+// local / retrieval / dense, and each head class has its own visible window
+// over a per-head page table): a query row at position i of request r sees
+//   GLOBAL, DENSE : j <= i
+//   LOCAL(W)      : j in [max(0, min(b_q, i - W + 1)), i]
+//   RETRIEVAL(S)  : j in [b_q, i]  U  [b_s, b_s + n_s) for the two chosen s
+// The table of (r, h) is the ascending list of pages holding any key some
+// query row of (r, h) sees; it is a union of at most three page intervals.
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define SEGKV_HD __host__ __device__ inline
+#else
+#define SEGKV_HD inline
+#endif
+
+namespace segkv {
+
+constexpr int kPage = 16;          // tokens per page
+constexpr int kTilePages = 4;      // pages per attention key tile
+constexpr int kTileKeys = kPage * kTilePages;
+constexpr int kMRows = 128;        // query rows per attention work-group (G heads x 128/G positions)
+constexpr int kMaxChunkTiles = 256;  // key tiles per work item (its page table is staged in LDS)
+constexpr int kClassGlobal = 0, kClassLocal = 1, kClassRetrieval = 2, kClassDense = 3;
+
+SEGKV_HD int cdiv(int a, int b) { return (a + b - 1) / b; }
+SEGKV_HD int imin(int a, int b) { return a < b ? a : b; }
+SEGKV_HD int imax(int a, int b) { return a > b ? a : b; }
+
+// Layout facts of one (request, kv head) pair, read from the metadata.
+struct HeadView {
+  int cls, W;
+  int bq, Lq, Lk;      // query segment start/length, context length
+  int rlo[2], rhi[2];  // retrieval segments [lo, hi) in tokens
+};
+
+// First visible key of a LOCAL row at position i.
+SEGKV_HD int local_lo(int i, int bq, int W) { return imax(0, imin(bq, i - W + 1)); }
+
+// Ascending, disjoint, non-adjacent page intervals [lo, hi).
+struct PageRuns {
+  int n;
+  int lo[3], hi[3];
+};
+
+SEGKV_HD PageRuns head_page_runs(const HeadView& v) {
+  PageRuns pr;
+  pr.n = 0;
+  const int last = cdiv(v.Lk, kPage);
+  if (v.cls == kClassLocal) {
+    pr.lo[0] = local_lo(v.bq, v.bq, v.W) / kPage;  // lo() is nondecreasing in i
+    pr.hi[0] = last;
+    pr.n = 1;
+  } else if (v.cls == kClassRetrieval) {
+    int lo[3] = {v.rlo[0] / kPage, v.rlo[1] / kPage, v.bq / kPage};
+    int hi[3] = {cdiv(v.rhi[0], kPage), cdiv(v.rhi[1], kPage), last};
+    // sort three intervals by lo (insertion sort), then merge touching ones
+    for (int a = 1; a < 3; ++a)
+      for (int b = a; b > 0 && lo[b] < lo[b - 1]; --b) {
+        int t = lo[b]; lo[b] = lo[b - 1]; lo[b - 1] = t;
+        t = hi[b]; hi[b] = hi[b - 1]; hi[b - 1] = t;
+      }
+    for (int a = 0; a < 3; ++a) {
+      if (pr.n > 0 && lo[a] <= pr.hi[pr.n - 1]) {
+        pr.hi[pr.n - 1] = imax(pr.hi[pr.n - 1], hi[a]);
+      } else {
+        pr.lo[pr.n] = lo[a];
+        pr.hi[pr.n] = hi[a];
+        ++pr.n;
+      }
+    }
+  } else {
+    pr.lo[0] = 0;
+    pr.hi[0] = last;
+    pr.n = 1;
+  }
+  return pr;
+}
+
+SEGKV_HD int runs_count(const PageRuns& pr) {
+  int n = 0;
+  for (int a = 0; a < pr.n; ++a) n += pr.hi[a] - pr.lo[a];
+  return n;
+}
+
+// Number of table pages with page index < p.
+SEGKV_HD int runs_rank(const PageRuns& pr, int p) {
+  int n = 0;
+  for (int a = 0; a < pr.n; ++a) {
+    if (p <= pr.lo[a]) break;
+    n += imin(p, pr.hi[a]) - pr.lo[a];
+  }
+  return n;
+}
+
+// Logical page of table entry e (0 <= e < runs_count).
+SEGKV_HD int runs_page(const PageRuns& pr, int e) {
+  for (int a = 0; a < pr.n; ++a) {
+    int len = pr.hi[a] - pr.lo[a];
+    if (e < len) return pr.lo[a] + e;
+    e -= len;
+  }
+  return -1;
+}
+
+// Table entry range [e0, e1) (relative to the (r, h) table) that query rows at
+// positions [i_lo, i_hi] can see. Rows are never empty: e1 > e0.
+SEGKV_HD void mtile_entries(const HeadView& v, const PageRuns& pr, int i_lo, int i_hi, int* e0, int* e1) {
+  *e1 = runs_rank(pr, i_hi / kPage + 1);
+  *e0 = (v.cls == kClassLocal) ? runs_rank(pr, local_lo(i_lo, v.bq, v.W) / kPage) : 0;
+}
+
+// Query positions per m-tile for group size G (G divides kMRows).
+SEGKV_HD int mtile_positions(int G) { return kMRows / G; }
+
+// Split of an m-tile's n_tiles key tiles into chunks of at most S tiles, as
+// evenly as possible: the first n % k chunks take one tile more than the rest.
+SEGKV_HD int num_chunks(int n_tiles, int S) { return imax(1, cdiv(n_tiles, S)); }
+SEGKV_HD int chunk_tile_lo(int n_tiles, int n_chunks, int c) {
+  const int q = n_tiles / n_chunks, r = n_tiles - q * n_chunks;
+  return c * q + imin(c, r);
+}
+
+// ---- device plan layout (opaque to callers) ----
+struct PlanHeader {
+  int32_t n_mtiles, n_items, n_split, chunk_tiles;
+  int32_t n_partials, total_q_rows, max_tiles, reserved;
+  int32_t pad[8];
+};
+
+struct MTile {
+  int32_t r, h;
+  int32_t q_row0;        // global Q row of the m-tile's first position
+  int32_t n_pos;         // valid positions in this m-tile (<= kMRows / G)
+  int32_t pos0;          // absolute position of the first row (b_q + t0)
+  int32_t cls, W, bq;
+  int32_t e_begin, e_end;  // absolute table entries [e_begin, e_end)
+  int32_t n_tiles, n_chunks;
+  int32_t partial_base;  // first partial slot, -1 when the m-tile is not split
+  int32_t pad[3];
+};
+
+struct Item {
+  int32_t mtile, chunk;
+};
+
+struct PlanLayout {
+  size_t move_off_off;   // int32 [R*Hkv + 1]: first move of each (r, h)
+  size_t req_mt_off;     // int32 [R + 1]: first m-tile of each request
+  size_t mtiles_off, items_off, split_off, total;
+};
+
+SEGKV_HD size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+SEGKV_HD PlanLayout plan_layout(int n_pairs, int n_requests, int n_mtiles, int n_items, int n_split) {
+  PlanLayout L;
+  L.move_off_off = align256(sizeof(PlanHeader));
+  L.req_mt_off = L.move_off_off + align256(sizeof(int32_t) * (size_t)(n_pairs + 1));
+  L.mtiles_off = L.req_mt_off + align256(sizeof(int32_t) * (size_t)(n_requests + 1));
+  L.items_off = L.mtiles_off + align256(sizeof(MTile) * (size_t)imax(n_mtiles, 1));
+  L.split_off = L.items_off + align256(sizeof(Item) * (size_t)imax(n_items, 1));
+  L.total = L.split_off + align256(sizeof(int32_t) * (size_t)imax(n_split, 1));
+  return L;
+}
+
+// Bytes of one partial result slot: kMRows rows x (D fp32 O + m + l).
+SEGKV_HD size_t partial_slot_bytes(int D) { return (size_t)kMRows * (size_t)(D + 2) * sizeof(float); }
+
+}  // namespace segkv

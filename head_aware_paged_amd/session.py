@@ -1,0 +1,106 @@
+"""Buffer-owning convenience wrapper around the segkv C ABI.
+
+A ``SegPagedLayer`` holds one layer's layout (segments + head-class map), the
+device buffers the C calls write (page tables, move list, attention plan,
+split-KV workspace) and forwards to the binding. Buffers are torch tensors:
+PyTorch supplies device memory and streams; every computation happens in
+libsegkv's HIP kernels. The four calls mirror the adapter interface the RedKnot
+pages describe (paooo.com, "如何使用RedKnot"): ``build_pages`` is
+SELECTVISIBLESTATE, ``relocate`` the BUILDSTATE relocation, ``attention`` and
+``importance_topk``/``sparse_ffn`` the EXECUTE steps.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import (HostMeta, dims, rope_relocate, segkv_build_pages, segkv_plan_sizes, segkv_visible_spans,
+               segpaged_attn_prefill, sparse_ffn_swiglu, sparse_ffn_workspace_size, token_importance_topk)
+
+
+class SegPagedLayer:
+    def __init__(self, num_q_heads: int, num_kv_heads: int, head_dim: int, seg_indptr, seg_start, seg_len,
+                 head_class, window, retr_seg, page_size: int = 16, device: str = "cuda"):
+        self.meta = HostMeta(seg_indptr, seg_start, seg_len, head_class, window, retr_seg)
+        R = len(self.meta.seg_indptr) - 1
+        self.dims = dims(R, num_q_heads, num_kv_heads, head_dim, page_size, len(self.meta.seg_start))
+        self.sizes = segkv_plan_sizes(self.dims, self.meta)
+        self.device = device
+        self.dmeta = self.meta.to_device(device)
+        q_len = [int(self.meta.seg_len[self.meta.seg_indptr[r + 1] - 1]) for r in range(R)]
+        self.cu_q_host = np.concatenate([[0], np.cumsum(q_len)]).astype(np.int32)
+        self.cu_q = torch.from_numpy(self.cu_q_host).to(device)
+        i32 = dict(dtype=torch.int32, device=device)
+        n_tab = max(1, self.sizes["table_entries"])
+        self.page_indptr = torch.zeros(R * num_kv_heads + 1, **i32)
+        self.page_ids = torch.zeros(n_tab, **i32)
+        self.page_pos = torch.zeros(n_tab, **i32)
+        n_mv = max(1, self.sizes["move_entries"])
+        self.move_src = torch.zeros(n_mv, **i32)
+        self.move_dst = torch.zeros(n_mv, **i32)
+        self.move_delta = torch.zeros(n_mv, **i32)
+        self.plan = torch.zeros(self.sizes["plan_bytes"], dtype=torch.uint8, device=device)
+        ws = self.sizes["attn_workspace_bytes"]
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device) if ws > 0 else None
+        self.scale = 1.0 / math.sqrt(head_dim)
+
+    @property
+    def num_moves(self) -> int:
+        return int(self.sizes["move_entries"])
+
+    def build_pages(self, seg_page_indptr, seg_pages, cache_page_indptr=None, cache_pages=None,
+                    seg_orig_start=None, stream=None):
+        with_moves = cache_pages is not None
+        segkv_build_pages(self.dims, self.meta, self.dmeta, self.cu_q, seg_page_indptr, seg_pages,
+                          self.page_indptr, self.page_ids, self.page_pos, self.plan,
+                          cache_page_indptr, cache_pages, seg_orig_start,
+                          self.move_src if with_moves else None, self.move_dst if with_moves else None,
+                          self.move_delta if with_moves else None, stream=stream)
+
+    def visible_spans(self, stream=None):
+        spans = torch.empty(int(self.sizes["total_q_rows"]), self.dims.num_kv_heads, 3, 2, dtype=torch.int32,
+                            device=self.device)
+        segkv_visible_spans(self.dims, self.meta, self.dmeta, self.cu_q, spans, stream=stream)
+        return spans
+
+    def relocate(self, k_cache, k_work, v_cache, v_work, rope_theta: float, stream=None):
+        """Move the head-aware move list's pages from the cache pool to the working pool."""
+        rope_relocate(k_cache, k_work, v_cache, v_work, self.move_src, self.move_dst, self.move_delta,
+                      self.num_moves, self.dims.page_size, self.dims.head_dim, rope_theta, stream=stream)
+
+    def attention(self, q, k_pool, v_pool, out=None, lse=None, want_lse=True, stream=None):
+        T, Hq = int(self.sizes["total_q_rows"]), self.dims.num_q_heads
+        if out is None:
+            out = torch.empty(T, Hq, self.dims.head_dim, dtype=torch.bfloat16, device=self.device)
+        if lse is None and want_lse:
+            lse = torch.empty(T, Hq, dtype=torch.float32, device=self.device)
+        segpaged_attn_prefill(self.dims, self.meta, q, k_pool, v_pool, self.page_ids, self.page_pos, self.plan,
+                              self.scale, out, lse, self.workspace, stream=stream)
+        return out, lse
+
+    def importance_topk(self, q, k_pool, lse, n_last: int, k: Optional[Sequence[int]], importance=None,
+                        topk_idx=None, stream=None):
+        if importance is None:
+            importance = torch.empty(int(self.sizes["total_keys"]), dtype=torch.float32, device=self.device)
+        if k is not None and topk_idx is None:
+            topk_idx = torch.empty(max(1, int(sum(k))), dtype=torch.int32, device=self.device)
+        token_importance_topk(self.dims, self.meta, self.dmeta, self.cu_q, q, k_pool, self.page_indptr,
+                              self.page_ids, self.page_pos, lse, self.scale, n_last, k, importance,
+                              topk_idx if k is not None else None, stream=stream)
+        return importance, topk_idx
+
+
+class SparseFFN:
+    """Sparse SwiGLU FFN with its activation workspace sized for at most k_max rows."""
+
+    def __init__(self, w_gate, w_up, w_down, k_max: int):
+        self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
+        nbytes = sparse_ffn_workspace_size(k_max, w_gate.shape[0])
+        self.workspace = torch.empty(max(16, nbytes), dtype=torch.uint8, device=w_gate.device)
+
+    def __call__(self, hidden, idx, k: int, stream=None):
+        sparse_ffn_swiglu(hidden, idx, k, self.w_gate, self.w_up, self.w_down, self.workspace, stream=stream)
+        return hidden

@@ -1,0 +1,233 @@
+/*
+ * segkv — SegPagedAttention prefill on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libsegkv.so. The operations follow the four adapter calls the
+ * RedKnot pages describe (paooo.com, "如何使用RedKnot": BUILDSTATE,
+ * SELECTVISIBLESTATE, EXECUTE) and the runtime of the RedKnot README
+ * (topairepos.com, "About" and "Key Ideas": per-(layer, kv_head) head classes,
+ * per-head page tables over a segmented paged KV store, RoPE relocation of
+ * reused segment K, attention-importance token selection for a sparse FFN).
+ *
+ * Conventions shared by every entry point
+ *  - Every call returns an int32 status (SEGKV_OK or a negative error code);
+ *    segkv_status_string() names it and segkv_last_error() gives a
+ *    thread-local detail message. Nothing aborts, nothing throws across the
+ *    boundary.
+ *  - Arguments are validated on the host before anything is launched; a call
+ *    that returns an error has enqueued no GPU work.
+ *  - Device work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *    stream) and is asynchronous: no call synchronises the host.
+ *  - The caller owns and allocates every buffer. The library allocates no
+ *    device memory and keeps no device state between calls; scratch space is
+ *    passed in as `workspace`/`plan`.
+ *  - Pointers marked (host) are read synchronously during the call; (device)
+ *    pointers must be device memory, 16-byte aligned for bf16 tensors.
+ *  - bf16 tensors are raw 16-bit bfloat16 values. Token positions are
+ *    absolute positions within a request.
+ *  - Identical inputs give bitwise-identical outputs (no float atomics).
+ *  - Supported: head_dim 64 or 128, page_size 16, num_q_heads a multiple of
+ *    num_kv_heads with group size G = Hq/Hkv dividing 128.
+ */
+#ifndef SEGKV_H_
+#define SEGKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define SEGKV_OK 0
+#define SEGKV_ERR_INVALID_ARG (-1)   /* malformed shape, metadata or pointer */
+#define SEGKV_ERR_UNSUPPORTED (-2)   /* valid but not implemented (head_dim, page size, group size) */
+#define SEGKV_ERR_CAPACITY (-3)      /* an output buffer is too small */
+#define SEGKV_ERR_ALIGNMENT (-4)     /* a device pointer is not 16-byte aligned */
+#define SEGKV_ERR_WORKSPACE (-5)     /* workspace/plan buffer too small */
+#define SEGKV_ERR_HIP (-6)           /* a HIP runtime call failed (no device, launch failure) */
+
+/* ---- head classes (RedKnot README, "About": global / local / retrieval / dense) ----
+ * GLOBAL, DENSE : a query row at position i sees every key j <= i.
+ * LOCAL(W)      : its own (query) segment causally plus a causal sliding window
+ *                 of W keys that includes the row: j in [max(0, min(b_q, i-W+1)), i].
+ * RETRIEVAL(S)  : its own segment causally plus two chosen reused segments in full. */
+enum { SEGKV_GLOBAL = 0, SEGKV_LOCAL = 1, SEGKV_RETRIEVAL = 2, SEGKV_DENSE = 3 };
+
+typedef struct {
+  int32_t num_requests;   /* R */
+  int32_t num_q_heads;    /* Hq */
+  int32_t num_kv_heads;   /* Hkv; query head g reads kv head g / (Hq/Hkv) */
+  int32_t head_dim;       /* D: 64 or 128 */
+  int32_t page_size;      /* P: 16 */
+  int32_t num_segments;   /* S: total segments over all requests */
+} segkv_dims;
+
+/* Segment layout and head-class map. The same struct describes the host copy
+ * (validated, used for sizing) and the device copy (read by kernels); the two
+ * must hold identical values.
+ * Segment s of request r is listed in [seg_indptr[r], seg_indptr[r+1]); a
+ * request's segments are contiguous from position 0 (seg_start[first] = 0,
+ * seg_start[s+1] = seg_start[s] + seg_len[s]), every start is a multiple of
+ * page_size, and the LAST segment is the recomputed query segment (its rows
+ * are the request's query rows). Only the query segment may have a length
+ * that is not a multiple of page_size. */
+typedef struct {
+  const int32_t* seg_indptr;  /* [R+1] */
+  const int32_t* seg_start;   /* [S]  new (insertion) start b_s */
+  const int32_t* seg_len;     /* [S]  n_s > 0 */
+  const int8_t* head_class;   /* [R*Hkv] SEGKV_GLOBAL..SEGKV_DENSE, request-major */
+  const int32_t* window;      /* [R*Hkv] W > 0 for LOCAL heads, ignored otherwise */
+  const int32_t* retr_seg;    /* [R*Hkv*2] absolute segment ids for RETRIEVAL heads:
+                                 two distinct reused (non-query) segments of the same
+                                 request; ignored otherwise */
+} segkv_meta;
+
+/* Sizes implied by a layout, computed on the host (exact, not bounds). */
+typedef struct {
+  int64_t table_entries;   /* total page-table entries over all (request, kv head) */
+  int64_t move_entries;    /* head-aware relocation moves (table entries in reused segments) */
+  int64_t total_q_rows;    /* T_q = sum of query-segment lengths */
+  int64_t total_keys;      /* sum of context lengths L_k (importance vector length) */
+  size_t plan_bytes;       /* device plan buffer for segkv_build_pages / segpaged_attn_prefill */
+  size_t attn_workspace_bytes;  /* device workspace for segpaged_attn_prefill */
+} segkv_sizes;
+
+/* Status name ("SEGKV_OK", "SEGKV_ERR_INVALID_ARG", ...); static storage. */
+const char* segkv_status_string(int32_t status);
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* segkv_last_error(void);
+
+/* Validate a layout and compute its sizes. dims/meta/sizes: host. */
+int32_t segkv_plan_sizes(const segkv_dims* dims, const segkv_meta* meta_host, segkv_sizes* sizes);
+
+/*
+ * SELECTVISIBLESTATE — per-(request, kv head) page tables over the working store.
+ * (paooo.com "如何使用RedKnot": choose the reused local-head KV and the
+ * global-head ranges; README "About": per-head page table + segmented store.)
+ *
+ * For each (r, h), the table lists, in ascending position order, every page
+ * that holds at least one key visible to some query row of (r, h) under h's
+ * class. Entry e of (r, h) is at index page_indptr[r*Hkv+h] + e:
+ *   page_ids[e] = physical page in the working pool, page_pos[e] = position of
+ *   the page's first token.
+ * Working store layout: page q of segment s for kv head h is physical page
+ *   seg_pages[seg_page_indptr[s*Hkv+h] + q]        (device, int32)
+ * Optionally (move_src != NULL) it also writes the head-aware relocation move
+ * list: for each (r, h) in order and each table entry inside a reused segment,
+ *   move_src = cache page  cache_pages[cache_page_indptr[s*Hkv+h] + q],
+ *   move_dst = the working page, move_delta = b_s - seg_orig_start[s].
+ * Always writes the attention plan into `plan` (plan_bytes from
+ * segkv_plan_sizes), consumed by segpaged_attn_prefill.
+ * Capacities must be >= the exact sizes from segkv_plan_sizes (else
+ * SEGKV_ERR_CAPACITY). cu_q: [R+1] device prefix sums of query lengths.
+ */
+int32_t segkv_build_pages(const segkv_dims* dims, const segkv_meta* meta_host, const segkv_meta* meta_dev,
+                          const int32_t* cu_q_dev,
+                          const int32_t* seg_page_indptr_dev, const int32_t* seg_pages_dev,
+                          int32_t* page_indptr_dev, int32_t* page_ids_dev, int32_t* page_pos_dev,
+                          int64_t table_capacity,
+                          const int32_t* cache_page_indptr_dev, const int32_t* cache_pages_dev,
+                          const int32_t* seg_orig_start_dev,
+                          int32_t* move_src_dev, int32_t* move_dst_dev, int32_t* move_delta_dev,
+                          int64_t move_capacity,
+                          void* plan_dev, size_t plan_bytes, void* stream);
+
+/*
+ * Visible-span export (testing aid): for every query row and kv head, the
+ * row's visible key set as up to 3 maximal half-open intervals [lo, hi) of
+ * positions, ascending, padded with (-1, -1). spans: device int32
+ * [T_q][Hkv][3][2].
+ */
+int32_t segkv_visible_spans(const segkv_dims* dims, const segkv_meta* meta_host, const segkv_meta* meta_dev,
+                            const int32_t* cu_q_dev, int32_t* spans_dev, void* stream);
+
+/*
+ * BUILDSTATE relocation + page gather (README "About"/"Key Ideas": offline
+ * segment KV with RoPE relocation "for numerical alignment"; aitrends.kr
+ * "주요 기능").
+ * For each move m: K page dst_page[m] of k_dst = RoPE rotation by delta[m]
+ * positions of K page src_page[m] of k_src, and (if v_src != NULL) V page
+ * dst_page[m] of v_dst = copy of V page src_page[m] of v_src.
+ * Rotation: rotate-half pairs (j, j + D/2), angle delta * theta^(-2j/D);
+ * cos/sin from fp64, products in fp32, result rounded to bf16 (RNE).
+ * Pools: [pages][page_size][head_dim] bf16, k_src/v_src with src_pool_pages
+ * pages and k_dst/v_dst with dst_pool_pages pages. Moves with a page id out of
+ * range are skipped. In place (src page == dst page, same pool) is allowed;
+ * otherwise destinations must not overlap sources.
+ */
+int32_t rope_relocate(const void* k_src, void* k_dst, const void* v_src, void* v_dst,
+                      int64_t src_pool_pages, int64_t dst_pool_pages,
+                      const int32_t* src_page_dev, const int32_t* dst_page_dev, const int32_t* delta_dev,
+                      int32_t n_moves, int32_t page_size, int32_t head_dim, double rope_theta, void* stream);
+
+/*
+ * EXECUTE attention (paooo.com "RedKnot的技术原理": per-head paged storage with
+ * a fused varlen kernel and no attention mask; "如何使用RedKnot": global heads
+ * attend over the full range, local heads over reused paged KV).
+ * q:   [T_q][Hq][D] bf16, RoPE already applied; row cu_q[r] + t of request r
+ *      is the query at position b_q(r) + t.
+ * out: [T_q][Hq][D] bf16, softmax(scale * q k^T) v over the row's visible keys.
+ * lse: [T_q][Hq] fp32 natural-log sum of exp(scale * q k) over visible keys
+ *      (nullable).
+ * Keys are read only through the page tables written by segkv_build_pages for
+ * the same layout, whose plan must be passed in `plan`. k_pool/v_pool:
+ * [pool_pages][P][D] bf16. workspace: attn_workspace_bytes from
+ * segkv_plan_sizes (may be NULL when that is 0).
+ */
+int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_meta* meta_host,
+                              const void* q, const void* k_pool, const void* v_pool, int64_t pool_pages,
+                              const int32_t* page_ids_dev, const int32_t* page_pos_dev,
+                              const void* plan_dev, size_t plan_bytes,
+                              float softmax_scale, void* out, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * EXECUTE selection (README "About": Elastic Sparsity, token-selective FFN from
+ * attention importance; paooo.com "RedKnot的主要功能": top-k tokens by attention
+ * score take the dense FFN).
+ * importance[off_r + j] = sum over query heads g and the last n_last query rows
+ * i of request r of exp(scale * q_{g,i} . k_j - lse[i][g]) for visible j, else
+ * 0; off_r = sum of L_k over earlier requests, j in [0, L_k(r)). Summation
+ * order is fixed. lse: as written by segpaged_attn_prefill (device, required).
+ * topk_idx[koff_r + c], c < k[r]: the k[r] positions with the largest
+ * importance, ties to the lower position, in ascending order; koff_r = sum of
+ * k over earlier requests. k: host int32 [R], 0 <= k[r] <= L_k(r).
+ * Other arguments as in segpaged_attn_prefill. topk_idx may be NULL to skip
+ * selection.
+ */
+int32_t token_importance_topk(const segkv_dims* dims, const segkv_meta* meta_host, const segkv_meta* meta_dev,
+                              const int32_t* cu_q_dev, const void* q, const void* k_pool, int64_t pool_pages,
+                              const int32_t* page_indptr_dev, const int32_t* page_ids_dev,
+                              const int32_t* page_pos_dev, const float* lse_dev, float softmax_scale,
+                              int32_t n_last, const int32_t* k_host, float* importance_dev,
+                              int32_t* topk_idx_dev, void* stream);
+
+/*
+ * Top-k of one non-negative fp32 score vector (scores: device [n]): the k
+ * indices with the largest scores, ties to the lower index, ascending.
+ * Same selection rule as token_importance_topk. NaN and negative scores are
+ * not supported (SEGKV results unspecified).
+ */
+int32_t segkv_topk_select(const float* scores_dev, int32_t n, int32_t k, int32_t* idx_dev, void* stream);
+
+/*
+ * Sparse SwiGLU FFN (paooo.com "RedKnot的主要功能"/"RedKnot的技术原理": dense
+ * FFN for the selected tokens, identity residual for the rest).
+ * For every selected row i = idx[c], c < k:
+ *   hidden[i] <- bf16( hidden[i] + W_down . bf16( silu(W_gate . hidden[i]) * (W_up . hidden[i]) ) )
+ * with fp32 accumulation; all other rows are left untouched (in place).
+ * hidden: [n_rows][hidden_size] bf16; w_gate, w_up: [inter][hidden_size];
+ * w_down: [hidden_size][inter]; idx: device int32 [k], distinct, in range.
+ * hidden_size and inter must be multiples of 128. workspace:
+ * sparse_ffn_workspace_size(k, inter) bytes (the bf16 activation).
+ */
+size_t sparse_ffn_workspace_size(int32_t k, int32_t inter);
+int32_t sparse_ffn_swiglu(void* hidden, int32_t n_rows, int32_t hidden_size, int32_t inter,
+                          const int32_t* idx_dev, int32_t k, const void* w_gate, const void* w_up,
+                          const void* w_down, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SEGKV_H_ */

@@ -1,0 +1,95 @@
+"""GPU: attention-importance scores and top-k selection vs the fp64 oracle.
+
+Importance: relative error <= 1e-4. Top-k: bit-exact against the oracle's
+selection rule applied to the GPU's own importance vector, and against the
+fp64 selection except for swaps among keys within 1e-4 (relative) of the
+k-th value.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import build, i32
+
+pytestmark = pytest.mark.gpu
+
+G_, L_, R_, D_ = workloads.GLOBAL, workloads.LOCAL, workloads.RETRIEVAL, workloads.DENSE
+
+
+def run(w, n_last, k):
+    layer, dev = build(w)
+    _, lse = layer.attention(dev.q, dev.k_work, dev.v_work)
+    imp, idx = layer.importance_topk(dev.q, dev.k_work, lse, n_last, k)
+    torch.cuda.synchronize()
+    return imp.cpu().numpy(), (idx.cpu().numpy() if idx is not None else None)
+
+
+def check(w, imp_gpu, idx_gpu, n_last, k):
+    ref = oracle.importance(w, n_last=n_last)
+    off = koff = 0
+    for r, imp_r in enumerate(ref):
+        n = len(imp_r)
+        g = imp_gpu[off:off + n].astype(np.float64)
+        rel = np.abs(g - imp_r) / np.maximum(imp_r, 1e-30)
+        big = imp_r > 1e-6 * imp_r.max()
+        print(f"[{w.name} r{r}] importance max rel err {rel[big].max():.3e}", flush=True)
+        assert rel[big].max() <= 1e-4
+        assert np.all(np.abs(g - imp_r)[~big] <= 1e-4 * imp_r.max())
+        if idx_gpu is not None:
+            kr = k[r]
+            got = idx_gpu[koff:koff + kr]
+            # 1. the selection rule on the GPU's own scores (fp32 values, exact)
+            assert np.array_equal(got, oracle.topk_select(imp_gpu[off:off + n], kr))
+            # 2. vs the fp64 selection: only near-ties at the threshold may swap
+            exp = oracle.topk_select(imp_r, kr)
+            if kr > 0 and not np.array_equal(got, exp):
+                tau = np.sort(imp_r)[::-1][kr - 1]
+                diff = np.setxor1d(got, exp)
+                assert np.all(np.abs(imp_r[diff] - tau) <= 1e-4 * tau), diff
+                print(f"[{w.name} r{r}] near-tie swaps: {len(diff) // 2}", flush=True)
+            koff += kr
+        off += n
+
+
+def test_importance_topk_8k():
+    w = workloads.sparse_ffn_8k(with_ffn=False)
+    print("case sparse_ffn_8k: importance + top-k", flush=True)
+    imp, idx = run(w, 64, [w.topk])
+    check(w, imp, idx, 64, [w.topk])
+    assert abs(imp.astype(np.float64).sum() - 32 * 64) < 1e-2
+
+
+def test_zero_q_selects_lowest_indices():
+    w = workloads.sparse_ffn_8k(with_ffn=False)
+    w.q[:] = 0
+    print("case sparse_ffn_8k: Q=0 exact ties", flush=True)
+    imp, idx = run(w, 64, [w.topk])
+    assert np.all(imp[:8129] == imp[0])
+    assert np.array_equal(idx, np.arange(2048))
+
+
+def test_mixed_classes_multi_request():
+    w = workloads.make_custom("retr_mixed", Hq=8, Hkv=4, D=64, theta=1e4,
+                              seg_lens_per_req=[[64, 32, 48, 64, 27], [16, 16, 16]],
+                              orig_starts_per_req=[[5, 0, 100, 3, None], [0, 40, None]],
+                              classes=[R_, L_, G_, R_, D_, L_, R_, G_], windows=[0, 40, 0, 0, 0, 5, 0, 0],
+                              retr=[(2, 0), None, None, (1, 3), None, None, (0, 1), None])
+    print("case retr_mixed: importance + top-k, 2 requests, n_last 20", flush=True)
+    k = [50, 7]
+    imp, idx = run(w, 20, k)
+    check(w, imp, idx, 20, k)
+
+
+@pytest.mark.parametrize("n,k,levels", [(1000, 100, 7), (33280, 8320, 50), (4096, 4096, 3), (5, 1, 1),
+                                        (70000, 1, 0), (2049, 2048, 2)])
+def test_topk_select_ties(n, k, levels):
+    print(f"case topk n={n} k={k} levels={levels}", flush=True)
+    x = workloads.uniform_f32(seed=n + k, n=n, levels=levels)
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    from head_aware_paged_amd import segkv_topk_select
+    segkv_topk_select(torch.from_numpy(x).cuda(), n, k, idx)
+    torch.cuda.synchronize()
+    ref = sorted(sorted(range(n), key=lambda j: (-float(x[j]), j))[:k])
+    assert idx.cpu().numpy().tolist() == ref

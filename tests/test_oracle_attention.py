@@ -32,10 +32,10 @@ def _gather_by_token(w, r, h):
 
 def _retr_variant():
     return workloads.make_custom("tiny_retr", Hq=4, Hkv=4, D=64, theta=1e4,
-                                 seg_lens_per_req=[[64, 32, 48, 64, 27], [16, 16]],
-                                 orig_starts_per_req=[[5, 0, 100, 3, None], [0, None]],
+                                 seg_lens_per_req=[[64, 32, 48, 64, 27], [16, 16, 16]],
+                                 orig_starts_per_req=[[5, 0, 100, 3, None], [0, 40, None]],
                                  classes=[R_, L_, G_, R_, D_, L_, R_, G_], windows=[0, 40, 0, 0, 0, 5, 0, 0],
-                                 retr=[(2, 0), None, None, (1, 3), None, None, (0, 0), None])
+                                 retr=[(2, 0), None, None, (1, 3), None, None, (0, 1), None])
 
 
 @pytest.mark.parametrize("make", [workloads.tiny, lambda: workloads.tiny(window=8), _retr_variant])
@@ -104,10 +104,10 @@ def test_constant_v_and_zero_q():
     w = _retr_variant()
     c_bits = np.uint16(0x3FC0)  # bf16 1.5
     wc = workloads.make_custom("c", Hq=4, Hkv=4, D=64, theta=1e4,
-                               seg_lens_per_req=[[64, 32, 48, 64, 27], [16, 16]],
-                               orig_starts_per_req=[[5, 0, 100, 3, None], [0, None]],
+                               seg_lens_per_req=[[64, 32, 48, 64, 27], [16, 16, 16]],
+                               orig_starts_per_req=[[5, 0, 100, 3, None], [0, 40, None]],
                                classes=[R_, L_, G_, R_, D_, L_, R_, G_], windows=[0, 40, 0, 0, 0, 5, 0, 0],
-                               retr=[(2, 0), None, None, (1, 3), None, None, (0, 0), None])
+                               retr=[(2, 0), None, None, (1, 3), None, None, (0, 1), None])
     wc.v_work[:] = c_bits
     O, _ = oracle.attention(wc)
     np.testing.assert_allclose(O, 1.5, rtol=0, atol=1e-14)

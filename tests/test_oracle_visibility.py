@@ -27,10 +27,10 @@ def _variants():
     yield workloads.tiny()
     yield workloads.tiny(window=8)
     yield workloads.make_custom("tiny_retr", Hq=4, Hkv=4, D=64, theta=1e4,
-                                seg_lens_per_req=[[64, 32, 48, 64, 27], [16, 16]],
-                                orig_starts_per_req=[[5, 0, 100, 3, None], [0, None]],
+                                seg_lens_per_req=[[64, 32, 48, 64, 27], [16, 16, 16]],
+                                orig_starts_per_req=[[5, 0, 100, 3, None], [0, 40, None]],
                                 classes=[2, 1, 0, 2, 3, 1, 2, 0], windows=[0, 40, 0, 0, 0, 5, 0, 0],
-                                retr=[(2, 0), None, None, (1, 3), None, None, (0, 0), None])
+                                retr=[(2, 0), None, None, (1, 3), None, None, (0, 1), None])
 
 
 def test_brute_and_interval_visibility_agree():
@@ -127,5 +127,5 @@ def test_spans_and_moves():
     sp3 = oracle.visible_spans(w3)
     # request 0, head 0 is RETRIEVAL over segments 2 ([96,144)) and 0 ([0,64)); query at 208
     assert [tuple(x) for x in sp3[0, 0]] == [(0, 64), (96, 144), (208, 209)]
-    # request 1 head 2 (retrieval of segment 0 twice -> one segment), query at 16: [0,16) + [16,17) merge
-    assert [tuple(x) for x in sp3[27, 2]] == [(0, 17), (-1, -1), (-1, -1)]
+    # request 1 head 2: retrieval of both reused segments [0,16) and [16,32), query at 32 -> one span
+    assert [tuple(x) for x in sp3[27, 2]] == [(0, 33), (-1, -1), (-1, -1)]

@@ -217,7 +217,7 @@ def tiny(seed: int = 0, window: int = 32, fill_reused_work: bool = True, with_da
     move by 0, 64 and 128); classes per kv head are global, local(32),
     local(32), dense; RoPE theta 1e4.
     """
-    return make_custom("tiny_224", Hq=8, Hkv=4, D=64, theta=1e4,
+    return make_custom("tiny_224" if window == 32 else f"tiny_224_w{window}", Hq=8, Hkv=4, D=64, theta=1e4,
                        seg_lens_per_req=[[64, 64, 64, 32]], orig_starts_per_req=[[0, 0, 0, None]],
                        classes=[GLOBAL, LOCAL, LOCAL, DENSE], windows=[0, window, window, 0],
                        seed=seed, fill_reused_work=fill_reused_work, with_data=with_data)
