@@ -59,93 +59,133 @@ struct PagesArgs {
   PlanLayout L;
 };
 
-// Table sizes -> page_indptr and move counts -> move offsets (block-wide).
-__device__ void table_offsets(const PagesArgs& a, int* s) {
-  const int n = a.R * a.Hkv;
-  int32_t* move_off = reinterpret_cast<int32_t*>(a.plan + a.L.move_off_off);
-  const int tot = block_exclusive_scan(
-      n,
-      [&](int k) {
-        const HeadView v = head_view_dev(a.m, a.Hkv, k / a.Hkv, k % a.Hkv);
-        return runs_count(head_page_runs(v));
-      },
-      [&](int k, int p) { a.page_indptr[k] = p; }, s);
-  const int mtot = block_exclusive_scan(
-      n,
-      [&](int k) {
-        const HeadView v = head_view_dev(a.m, a.Hkv, k / a.Hkv, k % a.Hkv);
-        return runs_rank(head_page_runs(v), v.bq / kPage);
-      },
-      [&](int k, int p) { move_off[k] = p; }, s);
-  if (threadIdx.x == 0) {
-    a.page_indptr[n] = tot;
-    move_off[n] = mtot;
-  }
-  __syncthreads();
-}
+constexpr int kMaxPairs = 1024;     // (request, kv head) pairs of one layout
+constexpr int kMaxMTiles = 8192;    // attention m-tiles of one layout
 
-// Grid (pair, entry block): fill 256 table entries of pair (r, h) and their moves.
-__global__ __launch_bounds__(256) void table_fill_kernel(PagesArgs a) {
-  const int k = blockIdx.x;
+// Per-pair facts, staged in LDS once.
+struct PairInfo {
+  int cls, W, bq, Lq, cu_q, tbase;
+  PageRuns pr;
+};
+
+__device__ PairInfo pair_info(const PagesArgs& a, int k) {
   const int r = k / a.Hkv, h = k % a.Hkv;
-  const int e = blockIdx.y * blockDim.x + threadIdx.x;
   const HeadView v = head_view_dev(a.m, a.Hkv, r, h);
-  const PageRuns pr = head_page_runs(v);
-  if (e >= runs_count(pr)) return;
-  const int base = a.page_indptr[k];
-  const int32_t* move_off = reinterpret_cast<const int32_t*>(a.plan + a.L.move_off_off);
-  const int s0 = a.m.seg_indptr[r], s1 = a.m.seg_indptr[r + 1];
-  const int p = runs_page(pr, e);
-  const int tok = p * kPage;
-  // segment holding this page: last segment with start <= tok
-  int lo = s0, hi = s1 - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.m.seg_start[mid] <= tok) lo = mid; else hi = mid - 1;
-  }
-  const int s = lo;
-  const int qpage = (tok - a.m.seg_start[s]) / kPage;
-  const int phys = a.seg_pages[a.seg_page_indptr[s * a.Hkv + h] + qpage];
-  a.page_ids[base + e] = phys;
-  a.page_pos[base + e] = tok;
-  if (a.move_src != nullptr && s != s1 - 1) {
-    // reused pages precede the query segment's pages in the ascending table
-    const int mi = move_off[k] + e;
-    a.move_src[mi] = a.cache_pages[a.cache_page_indptr[s * a.Hkv + h] + qpage];
-    a.move_dst[mi] = phys;
-    a.move_delta[mi] = a.m.seg_start[s] - a.seg_orig_start[s];
-  }
+  PairInfo p;
+  p.cls = v.cls;
+  p.W = v.W;
+  p.bq = v.bq;
+  p.Lq = v.Lq;
+  p.cu_q = a.cu_q[r];
+  p.tbase = 0;
+  p.pr = head_page_runs(v);
+  return p;
 }
 
-// One block: table offsets, then the m-tile descriptors, partial slots, split
-// list and the item list ordered from the largest item to the smallest
-// (longest-first dispatch).
-__global__ __launch_bounds__(kScanThreads) void plan_kernel(PagesArgs a) {
+// One launch: block 0 plans, every other block fills up to 1024 table entries
+// of one (request, kv head) pair. A fill block derives its pair's CSR offsets
+// itself, so it does not wait for the planning block.
+__global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fill_blocks_per_pair) {
   __shared__ int s[kScanThreads];
   __shared__ int bins[1024];
+  __shared__ PairInfo info[kMaxPairs];
+  __shared__ int req_off[kMaxPairs + 1];
+  __shared__ int mt_tiles[kMaxMTiles];
+  __shared__ int mt_chunks[kMaxMTiles];
+  __shared__ int red[2][kScanThreads / 64];
+  __shared__ int n_items_s;
   const int tid = threadIdx.x;
-  table_offsets(a, s);
+  const int n_pairs = a.R * a.Hkv;
+
+  if (blockIdx.x > 0) {
+    // ---------------- table fill for pair k, entries [blk * 1024, ...) ----------------
+    const int k = (blockIdx.x - 1) / fill_blocks_per_pair;
+    const int blk = (blockIdx.x - 1) % fill_blocks_per_pair;
+    int tsum = 0, msum = 0;  // table sizes and move counts of the pairs before k
+    for (int q = tid; q < k; q += kScanThreads) {
+      const PairInfo p = pair_info(a, q);
+      tsum += runs_count(p.pr);
+      msum += runs_rank(p.pr, p.bq / kPage);
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      tsum += __shfl_xor(tsum, o);
+      msum += __shfl_xor(msum, o);
+    }
+    if ((tid & 63) == 0) {
+      red[0][tid >> 6] = tsum;
+      red[1][tid >> 6] = msum;
+    }
+    const PairInfo p = pair_info(a, k);
+    __syncthreads();
+    int base = 0, mbase = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      base += red[0][w];
+      mbase += red[1][w];
+    }
+    const int e = blk * kScanThreads + tid;
+    if (e >= runs_count(p.pr)) return;
+    const int r = k / a.Hkv, h = k % a.Hkv;
+    const int s0 = a.m.seg_indptr[r], s1 = a.m.seg_indptr[r + 1];
+    const int tok = runs_page(p.pr, e) * kPage;
+    int lo = s0, hi = s1 - 1;  // segment holding this page: last segment with start <= tok
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.m.seg_start[mid] <= tok) lo = mid; else hi = mid - 1;
+    }
+    const int sg = lo;
+    const int qpage = (tok - a.m.seg_start[sg]) / kPage;
+    const int phys = a.seg_pages[a.seg_page_indptr[sg * a.Hkv + h] + qpage];
+    a.page_ids[base + e] = phys;
+    a.page_pos[base + e] = tok;
+    if (a.move_src != nullptr && sg != s1 - 1) {
+      // reused pages precede the query segment's pages in the ascending table
+      const int mi = mbase + e;
+      a.move_src[mi] = a.cache_pages[a.cache_page_indptr[sg * a.Hkv + h] + qpage];
+      a.move_dst[mi] = phys;
+      a.move_delta[mi] = a.m.seg_start[sg] - a.seg_orig_start[sg];
+    }
+    return;
+  }
+
+  // ---------------- block 0: table offsets and the attention plan ----------------
   PlanHeader* hdr = reinterpret_cast<PlanHeader*>(a.plan);
-  int32_t* req_off = reinterpret_cast<int32_t*>(a.plan + a.L.req_mt_off);
+  int32_t* move_off = reinterpret_cast<int32_t*>(a.plan + a.L.move_off_off);
+  int32_t* req_off_g = reinterpret_cast<int32_t*>(a.plan + a.L.req_mt_off);
   MTile* mt = reinterpret_cast<MTile*>(a.plan + a.L.mtiles_off);
   Item* items = reinterpret_cast<Item*>(a.plan + a.L.items_off);
   int32_t* split = reinterpret_cast<int32_t*>(a.plan + a.L.split_off);
   const int MP = mtile_positions(a.G);
   const int S = a.chunk_tiles;
 
-  // m-tiles per request (Hkv heads x ceil(Lq / MP) position blocks)
-  const int n_mt = block_exclusive_scan(
-      a.R,
-      [&](int r) {
-        const int sq = a.m.seg_indptr[r + 1] - 1;
-        return a.Hkv * cdiv(a.m.seg_len[sq], MP);
+  for (int k = tid; k < n_pairs; k += kScanThreads) info[k] = pair_info(a, k);
+  __syncthreads();
+  const int tot = block_exclusive_scan(
+      n_pairs, [&](int k) { return runs_count(info[k].pr); },
+      [&](int k, int p) {
+        a.page_indptr[k] = p;
+        info[k].tbase = p;
       },
-      [&](int r, int p) { req_off[r] = p; }, s);
-  if (tid == 0) req_off[a.R] = n_mt;
+      s);
+  const int mtot = block_exclusive_scan(
+      n_pairs, [&](int k) { return runs_rank(info[k].pr, info[k].bq / kPage); },
+      [&](int k, int p) { move_off[k] = p; }, s);
+  const int n_mt = block_exclusive_scan(
+      a.R, [&](int r) { return a.Hkv * cdiv(info[r * a.Hkv].Lq, MP); },
+      [&](int r, int p) {
+        req_off[r] = p;
+        req_off_g[r] = p;
+      },
+      s);
+  if (tid == 0) {
+    a.page_indptr[n_pairs] = tot;
+    move_off[n_pairs] = mtot;
+    req_off[a.R] = n_mt;
+    req_off_g[a.R] = n_mt;
+  }
   __syncthreads();
 
   // descriptors, one m-tile per thread
-  for (int i = tid; i < n_mt; i += blockDim.x) {
+  for (int i = tid; i < n_mt; i += kScanThreads) {
     int lo = 0, hi = a.R - 1;  // request: last r with req_off[r] <= i
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -154,42 +194,48 @@ __global__ __launch_bounds__(kScanThreads) void plan_kernel(PagesArgs a) {
     const int r = lo;
     const int nj = (req_off[r + 1] - req_off[r]) / a.Hkv;
     const int h = (i - req_off[r]) / nj, j = (i - req_off[r]) % nj;
-    const HeadView v = head_view_dev(a.m, a.Hkv, r, h);
-    const PageRuns pr = head_page_runs(v);
-    const int base = a.page_indptr[r * a.Hkv + h];
+    const PairInfo& p = info[r * a.Hkv + h];
+    HeadView v;
+    v.cls = p.cls;
+    v.W = p.W;
+    v.bq = p.bq;
+    v.Lq = p.Lq;
+    v.Lk = p.bq + p.Lq;
     const int t0 = j * MP;
-    const int i_lo = v.bq + t0, i_hi = v.bq + imin(v.Lq, t0 + MP) - 1;
+    const int i_lo = p.bq + t0, i_hi = p.bq + imin(p.Lq, t0 + MP) - 1;
     int e0, e1;
-    mtile_entries(v, pr, i_lo, i_hi, &e0, &e1);
+    mtile_entries(v, p.pr, i_lo, i_hi, &e0, &e1);
     MTile d;
     d.r = r;
     d.h = h;
-    d.q_row0 = a.cu_q[r] + t0;
-    d.n_pos = imin(v.Lq, t0 + MP) - t0;
+    d.q_row0 = p.cu_q + t0;
+    d.n_pos = imin(p.Lq, t0 + MP) - t0;
     d.pos0 = i_lo;
-    d.cls = v.cls;
-    d.W = v.W;
-    d.bq = v.bq;
-    d.e_begin = base + e0;
-    d.e_end = base + e1;
+    d.cls = p.cls;
+    d.W = p.W;
+    d.bq = p.bq;
+    d.e_begin = p.tbase + e0;
+    d.e_end = p.tbase + e1;
     d.n_tiles = cdiv(e1 - e0, kTilePages);
     d.n_chunks = num_chunks(d.n_tiles, S);
     d.partial_base = -1;
     d.pad[0] = d.pad[1] = d.pad[2] = 0;
     mt[i] = d;
+    mt_tiles[i] = d.n_tiles;
+    mt_chunks[i] = d.n_chunks;
   }
   __syncthreads();
 
   const int n_partials = block_exclusive_scan(
-      n_mt, [&](int i) { return mt[i].n_chunks > 1 ? mt[i].n_chunks : 0; },
+      n_mt, [&](int i) { return mt_chunks[i] > 1 ? mt_chunks[i] : 0; },
       [&](int i, int p) {
-        if (mt[i].n_chunks > 1) mt[i].partial_base = p;
+        if (mt_chunks[i] > 1) mt[i].partial_base = p;
       },
       s);
   const int n_split = block_exclusive_scan(
-      n_mt, [&](int i) { return mt[i].n_chunks > 1 ? 1 : 0; },
+      n_mt, [&](int i) { return mt_chunks[i] > 1 ? 1 : 0; },
       [&](int i, int p) {
-        if (mt[i].n_chunks > 1) split[p] = i;
+        if (mt_chunks[i] > 1) split[p] = i;
       },
       s);
 
@@ -199,14 +245,10 @@ __global__ __launch_bounds__(kScanThreads) void plan_kernel(PagesArgs a) {
   // size classes: 1024 * (size - 1) / S fits in 32 bits because S <= 2^18 (contexts <= 2^24 tokens)
   auto size_bin = [&](int sz) { return 1023 - ((sz - 1) * 1024) / S; };
   for (int i = tid; i < n_mt; i += blockDim.x) {
-    const int nt = mt[i].n_tiles, nc = mt[i].n_chunks;
-    for (int c = 0; c < nc; ++c) {
-      const int sz = chunk_tile_lo(nt, nc, c + 1) - chunk_tile_lo(nt, nc, c);
-      atomicAdd(&bins[size_bin(sz)], 1);
-    }
+    const int nt = mt_tiles[i], nc = mt_chunks[i];
+    for (int c = 0; c < nc; ++c) atomicAdd(&bins[size_bin(chunk_tile_lo(nt, nc, c + 1) - chunk_tile_lo(nt, nc, c))], 1);
   }
   __syncthreads();
-  __shared__ int n_items_s;
   {  // bin counts -> start cursors (largest size class first), block-parallel
     const int c = bins[tid];
     s[tid] = c;
@@ -221,19 +263,17 @@ __global__ __launch_bounds__(kScanThreads) void plan_kernel(PagesArgs a) {
     if (tid == kScanThreads - 1) n_items_s = s[tid];
   }
   __syncthreads();
-  const int n_items = n_items_s;
   for (int i = tid; i < n_mt; i += blockDim.x) {
-    const int nt = mt[i].n_tiles, nc = mt[i].n_chunks;
+    const int nt = mt_tiles[i], nc = mt_chunks[i];
     for (int c = 0; c < nc; ++c) {
-      const int sz = chunk_tile_lo(nt, nc, c + 1) - chunk_tile_lo(nt, nc, c);
-      const int slot = atomicAdd(&bins[size_bin(sz)], 1);
+      const int slot = atomicAdd(&bins[size_bin(chunk_tile_lo(nt, nc, c + 1) - chunk_tile_lo(nt, nc, c))], 1);
       items[slot] = Item{i, c};
     }
   }
   if (tid == 0) {
     PlanHeader h;
     h.n_mtiles = n_mt;
-    h.n_items = n_items;
+    h.n_items = n_items_s;
     h.n_split = n_split;
     h.chunk_tiles = S;
     h.n_partials = n_partials;
@@ -329,6 +369,9 @@ extern "C" int32_t segkv_build_pages(const segkv_dims* dims, const segkv_meta* m
   if (plan_bytes < hp.plan_bytes)
     return fail(SEGKV_ERR_WORKSPACE, "plan buffer " + std::to_string(plan_bytes) + " < " +
                                          std::to_string(hp.plan_bytes));
+  if (dims->num_requests * dims->num_kv_heads > kMaxPairs)
+    return fail(SEGKV_ERR_UNSUPPORTED, "more than 1024 (request, kv head) pairs in one call");
+  if (hp.n_mtiles > kMaxMTiles) return fail(SEGKV_ERR_UNSUPPORTED, "more than 8192 attention m-tiles in one call");
   if (!aligned16(plan_dev)) return fail(SEGKV_ERR_ALIGNMENT, "plan buffer must be 16-byte aligned");
 
   PagesArgs a;
@@ -352,14 +395,13 @@ extern "C" int32_t segkv_build_pages(const segkv_dims* dims, const segkv_meta* m
   a.chunk_tiles = hp.chunk_tiles;
   a.L = plan_layout(a.R * a.Hkv, a.R, hp.n_mtiles, hp.n_items, hp.n_split);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  plan_kernel<<<1, kScanThreads, 0, s>>>(a);
-  SEGKV_LAUNCH_CHECK();
   int max_pages = 1;
   for (int r = 0; r < a.R; ++r) {
     const int sq = meta_host->seg_indptr[r + 1] - 1;
     max_pages = imax(max_pages, cdiv(meta_host->seg_start[sq] + meta_host->seg_len[sq], kPage));
   }
-  table_fill_kernel<<<dim3(a.R * a.Hkv, cdiv(max_pages, 256)), 256, 0, s>>>(a);
+  const int per_pair = cdiv(max_pages, kScanThreads);
+  build_kernel<<<1 + a.R * a.Hkv * per_pair, kScanThreads, 0, s>>>(a, per_pair);
   SEGKV_LAUNCH_CHECK();
   return SEGKV_OK;
 }

@@ -53,6 +53,7 @@ struct PageRuns {
 SEGKV_HD PageRuns head_page_runs(const HeadView& v) {
   PageRuns pr;
   pr.n = 0;
+  pr.lo[0] = pr.hi[0] = pr.lo[1] = pr.hi[1] = pr.lo[2] = pr.hi[2] = 0;
   const int last = cdiv(v.Lk, kPage);
   if (v.cls == kClassLocal) {
     pr.lo[0] = local_lo(v.bq, v.bq, v.W) / kPage;  // lo() is nondecreasing in i
@@ -67,14 +68,30 @@ SEGKV_HD PageRuns head_page_runs(const HeadView& v) {
         int t = lo[b]; lo[b] = lo[b - 1]; lo[b - 1] = t;
         t = hi[b]; hi[b] = hi[b - 1]; hi[b - 1] = t;
       }
-    for (int a = 0; a < 3; ++a) {
-      if (pr.n > 0 && lo[a] <= pr.hi[pr.n - 1]) {
-        pr.hi[pr.n - 1] = imax(pr.hi[pr.n - 1], hi[a]);
-      } else {
-        pr.lo[pr.n] = lo[a];
-        pr.hi[pr.n] = hi[a];
-        ++pr.n;
-      }
+    // merge (the three slots are written through constant indices only)
+    pr.lo[0] = lo[0];
+    pr.hi[0] = hi[0];
+    pr.n = 1;
+    pr.lo[1] = pr.hi[1] = pr.lo[2] = pr.hi[2] = 0;
+    if (lo[1] <= pr.hi[0]) {
+      pr.hi[0] = imax(pr.hi[0], hi[1]);
+    } else {
+      pr.lo[1] = lo[1];
+      pr.hi[1] = hi[1];
+      pr.n = 2;
+    }
+    if (pr.n == 1 && lo[2] <= pr.hi[0]) {
+      pr.hi[0] = imax(pr.hi[0], hi[2]);
+    } else if (pr.n == 2 && lo[2] <= pr.hi[1]) {
+      pr.hi[1] = imax(pr.hi[1], hi[2]);
+    } else if (pr.n == 1) {
+      pr.lo[1] = lo[2];
+      pr.hi[1] = hi[2];
+      pr.n = 2;
+    } else {
+      pr.lo[2] = lo[2];
+      pr.hi[2] = hi[2];
+      pr.n = 3;
     }
   } else {
     pr.lo[0] = 0;
@@ -84,30 +101,34 @@ SEGKV_HD PageRuns head_page_runs(const HeadView& v) {
   return pr;
 }
 
+// (fixed trip counts with guards, so the run arrays stay in registers)
 SEGKV_HD int runs_count(const PageRuns& pr) {
   int n = 0;
-  for (int a = 0; a < pr.n; ++a) n += pr.hi[a] - pr.lo[a];
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+    if (a < pr.n) n += pr.hi[a] - pr.lo[a];
   return n;
 }
 
 // Number of table pages with page index < p.
 SEGKV_HD int runs_rank(const PageRuns& pr, int p) {
   int n = 0;
-  for (int a = 0; a < pr.n; ++a) {
-    if (p <= pr.lo[a]) break;
-    n += imin(p, pr.hi[a]) - pr.lo[a];
-  }
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+    if (a < pr.n) n += imax(0, imin(p, pr.hi[a]) - pr.lo[a]);
   return n;
 }
 
 // Logical page of table entry e (0 <= e < runs_count).
 SEGKV_HD int runs_page(const PageRuns& pr, int e) {
-  for (int a = 0; a < pr.n; ++a) {
-    int len = pr.hi[a] - pr.lo[a];
-    if (e < len) return pr.lo[a] + e;
+  int page = -1;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const int len = a < pr.n ? pr.hi[a] - pr.lo[a] : 0;
+    if (page < 0 && e < len) page = pr.lo[a] + e;
     e -= len;
   }
-  return -1;
+  return page;
 }
 
 // Table entry range [e0, e1) (relative to the (r, h) table) that query rows at
