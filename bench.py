@@ -83,23 +83,26 @@ def source_hash(names):
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(w, pairs_per_row, n_rows):
-    """The fp64 oracle on a bounded sample of the same workload (first n_rows query rows)."""
-    import numpy as np
+def cpu_baseline(w, pairs_per_row, min_seconds):
+    """The fp64 oracle on the same workload: whole passes over every query row
+    (all heads) until at least min_seconds of host time have been spent."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
-    rows = list(range(n_rows))
-    t0 = time.perf_counter()
-    oracle.attention(w, rows=rows)
-    dt = time.perf_counter() - t0
-    flops = 4.0 * w.head_dim * float(sum(pairs_per_row[:n_rows]))
+    passes, dt = 0, 0.0
+    while passes == 0 or dt < min_seconds:
+        t0 = time.perf_counter()
+        oracle.attention(w)
+        dt += time.perf_counter() - t0
+        passes += 1
+    flops = 4.0 * w.head_dim * float(pairs_per_row.sum()) * passes
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 oracle attention on query rows 0..{n_rows - 1} of {w.total_q_rows} (all {w.num_q_heads} "
-                      f"q heads) of {w.name}: {flops / 1e9:.2f} GFLOP visible-pair in {dt:.2f} s"}
+            "sample": f"fp64 oracle attention (explicit per-head masks) over all {w.total_q_rows} query rows x "
+                      f"{w.num_q_heads} q heads of {w.name}, {passes} pass(es): {flops / 1e9:.1f} GFLOP of "
+                      f"visible pairs in {dt:.1f} s"}
 
 
 def main():
@@ -107,7 +110,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-rows", type=int, default=128)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum host time of the oracle baseline")
     ap.add_argument("--skip-extras", action="store_true", help="only the timed steps (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -150,41 +153,104 @@ def main():
     imp = torch.empty(Lk, dtype=torch.float32, device=dev)
     idx = torch.empty(ksel[0], dtype=torch.int32, device=dev)
 
-    ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-          for n in ("pages", "reloc", "attn", "imp", "end")}
+    phases = {
+        "pages": lambda: layer.build_pages(spi, sp, cpi, cp, sos),
+        "reloc": lambda: layer.relocate(k_cache, k_work, v_cache, v_work, w.rope_theta),
+        "attn": lambda: layer.attention(q, k_work, v_work, out=out, lse=lse),
+        "imp": lambda: layer.importance_topk(q, k_work, lse, n_last, ksel, importance=imp, topk_idx=idx),
+    }
 
-    def step(i=None):
-        e = (lambda n: ev[n][i].record()) if i is not None else (lambda n: None)
-        e("pages")
-        layer.build_pages(spi, sp, cpi, cp, sos)
-        e("reloc")
-        layer.relocate(k_cache, k_work, v_cache, v_work, w.rope_theta)
-        e("attn")
-        layer.attention(q, k_work, v_work, out=out, lse=lse)
-        e("imp")
-        layer.importance_topk(q, k_work, lse, n_last, ksel, importance=imp, topk_idx=idx)
-        e("end")
+    def step():
+        for fn in phases.values():
+            fn()
 
-    log(f"warmup {args.warmup}")
+    log(f"warmup {args.warmup} eager steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
+    ref = [t.clone() for t in (out, lse, imp, idx)]
+
+    # HIP graphs: the whole step, and each phase on its own. A replay runs the
+    # captured kernel launches with no host work and no launch gaps, as a
+    # serving loop runs a layer; every graph's outputs are checked against the
+    # eager step before anything is timed.
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    def check_outputs(what):
+        torch.cuda.synchronize()
+        for a, b in zip((out, lse, imp, idx), ref):
+            if not torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b):
+                raise RuntimeError(f"{what}: graph replay differs from the eager step")
+
+    graph = capture(step)
+    per_graph = 10  # calls of one phase per phase graph, so graph launch cost is amortised
+
+    def repeat(fn):
+        def run():
+            for _ in range(per_graph):
+                fn()
+        return run
+
+    pgraphs = {n: capture(repeat(fn)) for n, fn in phases.items()}
+    for t in (out, lse, imp, idx):
+        t.zero_()
+    graph.replay()
+    check_outputs("step graph")
+    for t in (out, lse, imp, idx):
+        t.zero_()
+    for n in phases:
+        pgraphs[n].replay()
+    check_outputs("phase graphs")
+
+    def time_graph(g, reps):
+        """Average GPU time of one replay, HIP events on the replaying stream."""
+        for _ in range(args.warmup):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_phase = {n: time_graph(g, max(args.steps // 2, 10)) / per_graph for n, g in pgraphs.items()}
+    t_pages, t_reloc, t_attn, t_imp = (t_phase[n] for n in ("pages", "reloc", "attn", "imp"))
+
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} graph-replayed steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
-
-    def avg_ms(a, b):
-        return sum(ev[a][i].elapsed_time(ev[b][i]) for i in range(args.steps)) / args.steps
-
-    t_pages, t_reloc = avg_ms("pages", "reloc"), avg_ms("reloc", "attn")
-    t_attn, t_imp = avg_ms("attn", "imp"), avg_ms("imp", "end")
+    # a plain 64 MiB device copy, the known-size reference for HBM byte counters
+    xa = torch.empty(32 << 20, dtype=torch.bfloat16, device=dev)
+    torch.empty_like(xa).copy_(xa)
+    torch.cuda.synchronize()
+    del xa
     attn_tflops = flops / (t_attn * 1e-3) / 1e12
-    log(f"step {ms_step:.3f} ms: pages {t_pages * 1e3:.1f} us, relocate {t_reloc * 1e3:.1f} us, "
-        f"attention {t_attn * 1e3:.1f} us ({attn_tflops:.1f} TFLOP/s), importance+topk {t_imp * 1e3:.1f} us")
+    log(f"step {ms_step:.3f} ms (graph), {ms_eager:.3f} ms eager: pages {t_pages * 1e3:.1f} us, relocate "
+        f"{t_reloc * 1e3:.1f} us, attention {t_attn * 1e3:.1f} us ({attn_tflops:.1f} TFLOP/s), importance+topk "
+        f"{t_imp * 1e3:.1f} us")
     ha_bytes = 2.0 * layer.num_moves * 16 * D * 2 * 2  # K+V pages, read + write
 
     result = {
@@ -192,7 +258,7 @@ def main():
         "value": flops * args.steps / elapsed / 1e12,
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": ms_step, "ms_per_step_eager": ms_eager, "step_mode": "hip_graph_replay",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "mistral7b_32k", "context": Lk, "query_rows": T, "q_heads": Hq,
@@ -281,8 +347,8 @@ def main():
         log(f"sparse FFN {result['sparse_ffn_8k']['tflops']:.1f} TFLOP/s")
         del hid, ffn
 
-        log(f"cpu baseline: oracle on {args.cpu_rows} rows")
-        result["cpu_baseline"] = cpu_baseline(w, per_row, args.cpu_rows)
+        log("cpu baseline: fp64 oracle on the same workload")
+        result["cpu_baseline"] = cpu_baseline(w, per_row, args.cpu_seconds)
         log(f"cpu baseline {result['cpu_baseline']['value'] * 1e3:.2f} GFLOP/s")
 
     print(json.dumps(result), flush=True)

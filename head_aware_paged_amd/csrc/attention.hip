@@ -10,8 +10,9 @@
 // of one kv head times 128/G consecutive query positions (128 rows), so every
 // K/V page staged in LDS serves all G heads of the group. The m-tile's visible
 // table entries are walked in tiles of 4 pages (64 keys); long ranges are split
-// into chunks whose partial (m, l, O) are merged by a second kernel. Items are
-// dispatched largest first.
+// into chunks whose partial (m, l, O) are merged by a second kernel. Items run
+// in an XCD-aware order: the m-tiles that read the same key chunk are launched
+// on one XCD, so the chunk's pages come from HBM once into that XCD's L2.
 //
 // Per wave (32 rows) and tile, with the gfx950 32x32x16 bf16 MFMA:
 //   S^T[key][row] = K[key][:] . Q[row][:]     (A = K from LDS, B = Q in VGPRs)
@@ -128,6 +129,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
   const Item* items = reinterpret_cast<const Item*>(a.plan + a.L.items_off);
   if ((int)blockIdx.x >= hdr->n_items) return;
   const Item it = items[blockIdx.x];
+  if (it.mtile < 0) return;  // empty slot of the XCD-aware order
   const MTile mt = mts[it.mtile];
   const int t_lo = chunk_tile_lo(mt.n_tiles, mt.n_chunks, it.chunk);
   const int t_hi = chunk_tile_lo(mt.n_tiles, mt.n_chunks, it.chunk + 1);

@@ -170,7 +170,7 @@ int32_t compute_host_plan(const segkv_dims* d, const segkv_meta* m, HostPlan* ou
   const int R = d->num_requests, Hkv = d->num_kv_heads;
   const int G = d->num_q_heads / Hkv;
   const int MP = mtile_positions(G);
-  std::vector<int> tiles;
+  std::vector<int> tiles, pair_of_mtile;
   for (int r = 0; r < R; ++r) {
     for (int h = 0; h < Hkv; ++h) {
       const HeadView v = head_view_host(*d, *m, r, h);
@@ -187,21 +187,35 @@ int32_t compute_host_plan(const segkv_dims* d, const segkv_meta* m, HostPlan* ou
         int e0, e1;
         mtile_entries(v, pr, i_lo, i_hi, &e0, &e1);
         tiles.push_back(cdiv(e1 - e0, kTilePages));
+        pair_of_mtile.push_back(r * Hkv + h);
       }
     }
   }
   REQUIRE(p.table_entries < (int64_t)1 << 31, SEGKV_ERR_UNSUPPORTED, "more than 2^31 table entries");
   p.n_mtiles = (int)tiles.size();
   p.chunk_tiles = choose_chunk_tiles(tiles, attention_slots());
+  int64_t positions = 0;  // group-major item positions (holes included)
+  for (size_t i0 = 0; i0 < tiles.size();) {
+    // the m-tiles of one (request, kv head) pair are consecutive
+    size_t i1 = i0;
+    int maxc = 0;
+    while (i1 < tiles.size() && pair_of_mtile[i1] == pair_of_mtile[i0]) {
+      maxc = std::max(maxc, num_chunks(tiles[i1], p.chunk_tiles));
+      ++i1;
+    }
+    positions += (int64_t)maxc * (int64_t)(i1 - i0);
+    i0 = i1;
+  }
   for (int t : tiles) {
     const int k = num_chunks(t, p.chunk_tiles);
-    p.n_items += k;
     p.max_tiles = std::max(p.max_tiles, t);
     if (k > 1) {
       ++p.n_split;
       p.n_partials += k;
     }
   }
+  REQUIRE(positions < (int64_t)1 << 30, SEGKV_ERR_UNSUPPORTED, "too many attention work items");
+  p.n_items = kXcds * (int)((positions + kXcds - 1) / kXcds);
   const PlanLayout L = plan_layout(R * Hkv, R, p.n_mtiles, p.n_items, p.n_split);
   p.plan_bytes = L.total;
   p.workspace_bytes = (size_t)p.n_partials * partial_slot_bytes(d->head_dim);

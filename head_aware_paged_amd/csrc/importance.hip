@@ -21,6 +21,7 @@ namespace segkv {
 namespace {
 
 constexpr int kImpThreads = 256;
+constexpr int kImpWaves = kImpThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct ImpArgs {
@@ -37,24 +38,30 @@ struct ImpArgs {
   int R, Hq, Hkv, G, n_last;
 };
 
-constexpr int kImpMaxHeads = 64;  // kv heads per request handled by one work-group
+constexpr int kImpMaxHeads = 64;  // kv heads per request (one 64-bit wave vote)
+constexpr int kImpMaxLse = 4096;  // Hq * (n_last rounded up to 32) values staged in LDS
 
+// One work-group per 64-key block of one request. Its work is a list of
+// (kv head with a page at this block, 32-row block) units; wave w takes the
+// contiguous unit range [U w / 4, U (w + 1) / 4), so blocks that several
+// heads see spread those heads over the waves. Those blocks sit at the end of
+// the context (the local windows), so work-groups are numbered from the last
+// block backwards and the heavy ones start first. K and Q fragments go from
+// memory straight into MFMA operand registers; the next unit's Q is in flight
+// while the current one computes. Units whose 32 rows see all 64 keys skip
+// every mask.
 template <int D>
 __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
   constexpr int KS = D / 16;
-  constexpr int KCH = D / 8;
-  constexpr int kStride = D + 8;
-  constexpr int KLOADS = kTileKeys * KCH / kImpThreads;
-  __shared__ uint16_t ks_[kTileKeys * kStride];
-  __shared__ float colsum[4][kTileKeys];
-  __shared__ float s_lse[kImpMaxHeads * 8 * 64 / 8];  // Hq * n_last <= 4096 values
-  __shared__ int s_pid[kImpMaxHeads][kTilePages];      // page of each head's table at this key block, -1 if none
+  __shared__ float s_lse[kImpMaxLse];
+  __shared__ int s_pid[kImpMaxHeads][kTilePages];  // page of each head's table at this key block, -1 if none
   __shared__ int s_cls[kImpMaxHeads], s_W[kImpMaxHeads];
+  __shared__ float colsum[kImpWaves][kTileKeys];
 
   const int r = blockIdx.y;
   const int sq = a.m.seg_indptr[r + 1] - 1;
   const int bq = a.m.seg_start[sq], Lq = a.m.seg_len[sq], Lk = bq + Lq;
-  const int kb0 = blockIdx.x * kTileKeys;
+  const int kb0 = (gridDim.x - 1 - blockIdx.x) * kTileKeys;
   if (kb0 >= Lk) return;
   int off = 0;  // output offset of request r: sum of earlier context lengths
   for (int rr = 0; rr < r; ++rr) {
@@ -62,11 +69,13 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
     off += a.m.seg_start[s2] + a.m.seg_len[s2];
   }
   const int n = imin(a.n_last, Lq);
-  const int nb_head = cdiv(n, 32);  // 32-row blocks per query head (rows padded per head)
-  const int nrb = a.G * nb_head;
+  const int nb_head = cdiv(n, 32);  // 32-row blocks per query head
+  const int NP = 32 * nb_head;      // staged rows per query head (the last row repeated)
+  const int R8 = a.G * nb_head;     // units per kv head
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lrow = lane & 31, lg = lane >> 5;
   const int q_base = a.cu_q[r] + Lq - n;  // first of the last n query rows
+  const int pos_base = Lk - n;            // its position
 
   // ---- everything per head that does not depend on the rows, loaded once ----
   for (int x = tid; x < a.Hkv * kTilePages; x += kImpThreads) {
@@ -86,100 +95,117 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
       s_W[h] = v.W;
     }
   }
-  // log2-scaled LSE of the last n rows, [g][t]: all loads of a thread are
-  // issued before its stores (a plain loop would wait once per iteration)
-  for (int x0 = 0; x0 < a.Hq * n; x0 += 8 * kImpThreads) {
+  // log2-scaled LSE of the last n rows, [g][t] with t < NP (rows past n repeat
+  // row n - 1); all loads of a thread are issued before its stores
+  for (int x0 = 0; x0 < a.Hq * NP; x0 += 8 * kImpThreads) {
     float v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int x = x0 + u * kImpThreads + tid;
-      v[u] = x < a.Hq * n ? a.lse[(size_t)(q_base + x % n) * a.Hq + x / n] : 0.f;
+      v[u] = x < a.Hq * NP ? a.lse[(size_t)(q_base + imin(x % NP, n - 1)) * a.Hq + x / NP] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int x = x0 + u * kImpThreads + tid;
-      if (x < a.Hq * n) s_lse[x] = v[u] * kLog2e;
+      if (x < a.Hq * NP) s_lse[x] = v[u] * kLog2e;
     }
   }
   __syncthreads();
 
-  float acc0 = 0.f, acc1 = 0.f;  // keys lrow and 32 + lrow, this lane's rows
-  auto active = [&](int h) {
-    return s_pid[h][0] >= 0 || s_pid[h][1] >= 0 || s_pid[h][2] >= 0 || s_pid[h][3] >= 0;
-  };
-  u32x4 kreg[KLOADS];
-  auto load_k = [&](int h) {
-#pragma unroll
-    for (int u = 0; u < KLOADS; ++u) {
-      const int qd = tid + u * kImpThreads;
-      const int key = qd / KCH, c = qd % KCH;
-      const int pid = s_pid[h][key >> 4];
-      kreg[u] = pid >= 0 ? *reinterpret_cast<const u32x4*>(a.k_pool + ((size_t)pid * kPage + (key & 15)) * D + 8 * c)
-                         : u32x4{0, 0, 0, 0};
-    }
-  };
-  int h = 0;
-  while (h < a.Hkv && !active(h)) ++h;
-  if (h < a.Hkv) load_k(h);
-  while (h < a.Hkv) {
-    int h_next = h + 1;
-    while (h_next < a.Hkv && !active(h_next)) ++h_next;
-    __syncthreads();  // previous head's LDS reads are done
-#pragma unroll
-    for (int u = 0; u < KLOADS; ++u) {
-      const int qd = tid + u * kImpThreads;
-      *reinterpret_cast<u32x4*>(&ks_[(qd / KCH) * kStride + 8 * (qd % KCH)]) = kreg[u];
-    }
-    __syncthreads();
-    if (h_next < a.Hkv) load_k(h_next);  // lands while this head computes
+  // heads with a page at this key block (the same vote in every wave)
+  const bool on = lane < a.Hkv && (s_pid[lane][0] >= 0 || s_pid[lane][1] >= 0 || s_pid[lane][2] >= 0 ||
+                                   s_pid[lane][3] >= 0);
+  const uint64_t act = __ballot(on);
+  const int U = __popcll(act) * R8;
+  const int u_lo = (int)((int64_t)U * wave / kImpWaves), u_hi = (int)((int64_t)U * (wave + 1) / kImpWaves);
 
-    const int cls = s_cls[h], W = s_W[h];
-    const int pa = (lrow >> 4) ? s_pid[h][1] : s_pid[h][0], pb = (lrow >> 4) ? s_pid[h][3] : s_pid[h][2];
-    const int j0 = pa < 0 ? INT_MAX : kb0 + (lrow >> 4) * kPage + (lrow & 15);
-    const int j1 = pb < 0 ? INT_MAX : kb0 + 2 * kPage + (lrow >> 4) * kPage + (lrow & 15);
-    for (int rb = wave; rb < nrb; rb += 4) {
-      const int hg = rb / nb_head, tb = (rb % nb_head) * 32;
-      // A operand: Q of row tb + lrow of head hg (rows past n are clamped, masked below)
-      const uint16_t* qp = a.q + ((size_t)(q_base + imin(tb + lrow, n - 1)) * a.Hq + h * a.G + hg) * D + 8 * lg;
-      bf16x8 qf[KS];
+  float acc0 = 0.f, acc1 = 0.f;  // keys lrow and 32 + lrow, this lane's rows
+  bf16x8 kf[2][KS], qa[KS], qb[KS];
+  uint64_t rest = act;
+  for (int hi = 0; hi < u_lo / R8; ++hi) rest &= rest - 1;  // drop heads before the wave's first unit
+  int u = u_lo;
+  while (u < u_hi) {
+    const int hh = __builtin_ctzll(rest);
+    rest &= rest - 1;
+    const int u_end = imin(u_hi, (u / R8 + 1) * R8);
+    // B operand: key 32 kb + lrow, dims 16 ks + 8 lg .. + 8
 #pragma unroll
-      for (int kstep = 0; kstep < KS; ++kstep) qf[kstep] = *reinterpret_cast<const bf16x8*>(qp + 16 * kstep);
-      f32x16 s[2];
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = 32 * kb + lrow;
+      const int pid = s_pid[hh][key >> 4];
+      const uint16_t* kp = a.k_pool + ((size_t)imax(pid, 0) * kPage + (key & 15)) * D + 8 * lg;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = pid >= 0 ? *reinterpret_cast<const bf16x8*>(kp + 16 * ks) : bf16x8{};
+    }
+    const int cls = s_cls[hh], W = s_W[hh];
+    const bool pages_full = s_pid[hh][0] >= 0 && s_pid[hh][1] >= 0 && s_pid[hh][2] >= 0 && s_pid[hh][3] >= 0;
+    const int pa = s_pid[hh][lrow >> 4], pb = s_pid[hh][2 + (lrow >> 4)];
+    const int j0 = pa < 0 ? INT_MAX : kb0 + lrow;
+    const int j1 = pb < 0 ? INT_MAX : kb0 + 32 + lrow;
+
+    auto q_load = [&](bf16x8* dst, int uu) {  // A operand: Q row tb + lrow of head hg
+      const int rb = uu % R8, hg = rb / nb_head, tb = (rb % nb_head) * 32;
+      const uint16_t* qp = a.q + ((size_t)(q_base + imin(tb + lrow, n - 1)) * a.Hq + hh * a.G + hg) * D + 8 * lg;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+      for (int ks = 0; ks < KS; ++ks) dst[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
+    };
+    auto unit = [&](const bf16x8* qf, int uu) {
+      f32x16 s0, s1;
 #pragma unroll
-      for (int kstep = 0; kstep < KS; ++kstep)
+      for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks_[(32 * kb + lrow) * kStride + 16 * kstep + 8 * lg]);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[kstep], kf, s[kb], 0, 0, 0);
-        }
-      // lane holds keys (j0, j1) for rows t = tb + 8(i/4) + 4 lg + i%4 of head hg
-      const float* lse_h = &s_lse[(h * a.G + hg) * n];
+      for (int ks = 0; ks < KS; ++ks) {
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[0][ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[1][ks], s1, 0, 0, 0);
+      }
+      // lane holds keys (j0, j1) for rows t = tb + 8(i/4) + 4 lg + i%4 of query head hg
+      const int rb = uu % R8, hg = rb / nb_head, tb = (rb % nb_head) * 32;
+      const float* lse_h = &s_lse[(hh * a.G + hg) * NP + tb + 4 * lg];
+      f32x4 l2[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) l2[c] = *reinterpret_cast<const f32x4*>(lse_h + 8 * c);
+      const int pos0 = pos_base + tb;  // position of row tb
+      const bool full = pages_full && tb + 32 <= n && kb0 + kTileKeys - 1 <= pos0 &&
+                        (cls != kClassLocal || kb0 >= local_lo(pos0 + 31, bq, W));
       float p0 = 0.f, p1 = 0.f;
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int t = tb + 8 * (i >> 2) + 4 * lg + (i & 3);
-        const bool row_ok = t < n;
-        const int pos = bq + Lq - n + t;
-        const int lo = cls == kClassLocal ? local_lo(pos, bq, W) : 0;
-        const float l2 = lse_h[imin(t, n - 1)];
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[0][i], a.scale_log2, -l2));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[1][i], a.scale_log2, -l2));
-        p0 += (row_ok && j0 <= pos && j0 >= lo) ? e0 : 0.f;
-        p1 += (row_ok && j1 <= pos && j1 >= lo) ? e1 : 0.f;
+        for (int i = 0; i < 16; ++i) {
+          p0 += __builtin_amdgcn_exp2f(fmaf(s0[i], a.scale_log2, -l2[i >> 2][i & 3]));
+          p1 += __builtin_amdgcn_exp2f(fmaf(s1[i], a.scale_log2, -l2[i >> 2][i & 3]));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int t = tb + 8 * (i >> 2) + 4 * lg + (i & 3);
+          const bool row_ok = t < n;
+          const int pos = pos_base + t;
+          const int lo = cls == kClassLocal ? local_lo(pos, bq, W) : 0;
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(s0[i], a.scale_log2, -l2[i >> 2][i & 3]));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(s1[i], a.scale_log2, -l2[i >> 2][i & 3]));
+          p0 += (row_ok && j0 <= pos && j0 >= lo) ? e0 : 0.f;
+          p1 += (row_ok && j1 <= pos && j1 >= lo) ? e1 : 0.f;
+        }
       }
       acc0 += p0;
       acc1 += p1;
+    };
+
+    // two units per trip, Q buffers alternating without copies; the prefetches
+    // are unconditional (clamped to the last unit) so every wait before an
+    // MFMA can leave the other buffer's loads in flight
+    q_load(qa, u);
+    for (; u < u_end; u += 2) {
+      q_load(qb, imin(u + 1, u_end - 1));
+      unit(qa, u);
+      q_load(qa, imin(u + 2, u_end - 1));
+      if (u + 1 < u_end) unit(qb, u + 1);
     }
-    h = h_next;
+    u = u_end;
   }
   // lanes lg = 0 / 1 hold different rows of the same keys; then waves in order
   acc0 += __shfl_xor(acc0, 32);
   acc1 += __shfl_xor(acc1, 32);
-  __syncthreads();
   if (lg == 0) {
     colsum[wave][lrow] = acc0;
     colsum[wave][32 + lrow] = acc1;
@@ -187,134 +213,271 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
   __syncthreads();
   if (tid < kTileKeys) {
     const int j = kb0 + tid;
-    if (j < Lk) a.importance[off + j] = ((colsum[0][tid] + colsum[1][tid]) + colsum[2][tid]) + colsum[3][tid];
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kImpWaves; ++w) sum += colsum[w][tid];
+    if (j < Lk) a.importance[off + j] = sum;
   }
 }
 
+// ---- top-k: radix select on order-preserving integer keys ----
+//
+// One 1024-thread work-group selects the top k of one score vector. Wave w
+// owns the contiguous key range [256 S w, 256 S (w + 1)); inside it, sub-block
+// u holds keys 256 u + 4 lane + e (e < 4), kept in registers for every pass.
+// Four 8-bit digit passes find the k-th largest key; each pass counts the
+// candidates' digits in 64 lane-private LDS histograms (bin b of lane l at
+// 64 b + l, so a wave's increments never share a bank or an address) and
+// picks the digit with a suffix scan. One ordered compaction then writes
+// every key above the threshold and the lowest-indexed keys equal to it.
 constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kTopkSub = 256;  // keys per wave sub-block (64 lanes x 4)
+constexpr int kTopkMaxRegSub = 15;  // register-resident up to 15 x 256 x 16 = 61440 keys (no spills)
 
-// One work-group selects the top k of one score vector. Vectors of up to
-// kTopkCache keys are first copied into LDS, so the four radix passes and the
-// compaction read LDS; longer ones are streamed from memory on every pass.
-constexpr int kTopkCache = 36864;  // 144 KiB of fp32 keys
+// fp32 bit pattern -> unsigned integer of the same order (-0 ranks as +0)
+__device__ __forceinline__ uint32_t ordered_bits(uint32_t b) {
+  b = b == 0x80000000u ? 0u : b;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int32_t* idx_out, int n,
-                                                            int k) {
-  __shared__ uint32_t cache[kTopkCache];
-  __shared__ int hist[256];
-  __shared__ int s_scan[256];
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_krem;
-  __shared__ int wcnt[2][kTopkThreads / 64][2];
-  if (k <= 0) return;
-  const uint32_t* bits = reinterpret_cast<const uint32_t*>(scores);
-  const int tid = threadIdx.x;
-  const bool cached = n <= kTopkCache;
-  if (cached) {
-    // all loads of a thread in flight together (kTopkCache / 4 / kTopkThreads = 9 vectors at most)
-    const int n4 = (reinterpret_cast<uintptr_t>(bits) & 15) == 0 ? n / 4 : 0;
-    constexpr int V = (kTopkCache / 4 + kTopkThreads - 1) / kTopkThreads;
-    u32x4 v[V];
-#pragma unroll
-    for (int u = 0; u < V; ++u) {
-      const int x = u * kTopkThreads + tid;
-      if (x < n4) v[u] = reinterpret_cast<const u32x4*>(bits)[x];
-    }
-#pragma unroll
-    for (int u = 0; u < V; ++u) {
-      const int x = u * kTopkThreads + tid;
-      if (x < n4) reinterpret_cast<u32x4*>(cache)[x] = v[u];
-    }
-    for (int j = 4 * n4 + tid; j < n; j += kTopkThreads) cache[j] = bits[j];
-    __syncthreads();
+// Keys 4 lane + e of sub-block u; positions past n read as 0, below every real key.
+__device__ __forceinline__ u32x4 topk_load4(const uint32_t* bits, int j, int n, bool vec) {
+  u32x4 x;
+  if (vec && j + 3 < n) {
+    x = *reinterpret_cast<const u32x4*>(bits + j);
+  } else {
+    x[0] = j < n ? bits[j] : 0u;
+    x[1] = j + 1 < n ? bits[j + 1] : 0u;
+    x[2] = j + 2 < n ? bits[j + 2] : 0u;
+    x[3] = j + 3 < n ? bits[j + 3] : 0u;
   }
-  auto key_at = [&](int j) { return cached ? cache[j] : bits[j]; };
-  const int rounds = cdiv(n, kTopkThreads);
-  uint32_t prefix = 0, mask = 0;
+  u32x4 o;
+  o[0] = j < n ? ordered_bits(x[0]) : 0u;
+  o[1] = j + 1 < n ? ordered_bits(x[1]) : 0u;
+  o[2] = j + 2 < n ? ordered_bits(x[2]) : 0u;
+  o[3] = j + 3 < n ? ordered_bits(x[3]) : 0u;
+  return o;
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// S > 0: S sub-blocks per wave held in registers; S == 0: ns_rt sub-blocks
+// re-read from memory in every pass (vectors too long for registers; the
+// unroll pragmas below then do not apply).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wpass-failed"
+// DPP moves inside rows of 16 lanes; a lane whose source lies outside its row reads 0
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppRowShl4 = 0x104, kDppRowShl8 = 0x108;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+template <int S>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
+                                                            int32_t* __restrict__ idx_out, int n, int k, int ns_rt) {
+  __shared__ uint32_t hist[256 * 64];  // reused to stage the output indices when k <= 16384
+  __shared__ uint32_t s_wsum[kTopkWaves];
+  __shared__ uint32_t s_sel[3];
+  __shared__ int s_tot[kTopkWaves][2];
+  constexpr int SR = S > 0 ? S : 1;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ns = S > 0 ? S : ns_rt;
+  const int base = wave * ns * kTopkSub + 4 * lane;
+  const uint32_t* bits = reinterpret_cast<const uint32_t*>(scores);
+  const bool vec = (reinterpret_cast<uintptr_t>(bits) & 15) == 0;
+  u32x4 reg[SR];
+  if constexpr (S > 0) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) reg[u] = topk_load4(bits, base + kTopkSub * u, n, vec);
+  }
+#define SEGKV_TOPK_KEYS(u) (S > 0 ? reg[(S > 0 ? (u) : 0)] : topk_load4(bits, base + kTopkSub * (u), n, vec))
+
+  for (int x = tid; x < 256 * 64 / 4; x += kTopkThreads) reinterpret_cast<u32x4*>(hist)[x] = u32x4{0, 0, 0, 0};
+  __syncthreads();
+  uint32_t prefix = 0, eqc = 0;  // eqc: keys equal to the digits fixed so far
   int krem = k;
+#pragma unroll 1
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-#pragma unroll 4
-    for (int w = 0; w < rounds; ++w) {  // uniform trip count: wave votes stay converged
-      const int j = tid + w * kTopkThreads;
-      const uint32_t key = j < n ? key_at(j) : 0u;
-      const bool in = j < n && (key & mask) == prefix;
-      const uint32_t bin = (key >> shift) & 255u;
-      // skewed digits (the exponent byte) would serialise 64 lanes on one LDS
-      // counter: a wave whose candidates all share one bin adds them at once
-      const uint32_t b0 = __builtin_amdgcn_readfirstlane(in ? bin : 256u);
-      const uint64_t cand = __ballot(in);
-      const uint64_t same = __ballot(in && bin == b0);
-      if (cand != 0 && same == cand) {
-        if (__lane_id() == (uint32_t)__builtin_ctzll(cand)) atomicAdd(&hist[b0], (int)__popcll(cand));
-      } else if (in) {
-        atomicAdd(&hist[bin], 1);
-      }
+    const uint32_t fixed = pass == 0 ? 0u : 0xFFFFFFFFu << (shift + 8);  // digits chosen by earlier passes
+#pragma unroll
+    for (int u = 0; u < (S > 0 ? S : ns); ++u) {
+      const u32x4 x = SEGKV_TOPK_KEYS(u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((x[e] & fixed) == prefix) atomicAdd(&hist[(((x[e] >> shift) & 255u) << 6) + lane], 1u);
     }
     __syncthreads();
-    // digit holding the krem-th largest candidate: suffix sums over the 256 bins
-    const int c = tid < 256 ? hist[tid] : 0;
-    if (tid < 256) s_scan[tid] = c;
+    // bin totals: each lane of a quad sums, and clears for the next pass, 16 of
+    // the bin's 64 copies; the 16-byte pieces are visited in an order rotated
+    // by the bin, so the 16 lanes of a row (4 bins x 4 parts) cover all 64 banks
+    const int bin = tid >> 2, part = tid & 3;
+    u32x4* hp = reinterpret_cast<u32x4*>(hist + bin * 64 + 16 * part);
+    const u32x4 h0 = hp[bin & 3], h1 = hp[(bin + 1) & 3], h2 = hp[(bin + 2) & 3], h3 = hp[(bin + 3) & 3];
+    hp[bin & 3] = hp[(bin + 1) & 3] = hp[(bin + 2) & 3] = hp[(bin + 3) & 3] = u32x4{0, 0, 0, 0};
+    uint32_t c = ((h0[0] + h0[1]) + (h0[2] + h0[3])) + ((h1[0] + h1[1]) + (h1[2] + h1[3])) +
+                 ((h2[0] + h2[1]) + (h2[2] + h2[3])) + ((h3[0] + h3[1]) + (h3[2] + h3[3]));
+    c += dpp_move<kDppQuadXor1>(c);
+    c += dpp_move<kDppQuadXor2>(c);
+    // candidates with digit >= bin: suffix over the 4 bins of a 16-lane row,
+    // then the rows above in this wave, then the waves above
+    uint32_t sfx = c + dpp_move<kDppRowShl4>(c);
+    sfx += dpp_move<kDppRowShl8>(sfx);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 48);
+    const int row = lane >> 4;
+    sfx += (row < 1 ? r1 : 0u) + (row < 2 ? r2 : 0u) + (row < 3 ? r3 : 0u);
+    if (lane == 0) s_wsum[wave] = sfx;  // lane 0 holds the wave's total
     __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {  // inclusive suffix sum (bins above and including tid)
-      const int t = (tid < 256 && tid + o < 256) ? s_scan[tid + o] : 0;
-      __syncthreads();
-      if (tid < 256) s_scan[tid] += t;
-      __syncthreads();
+    uint32_t above = 0;
+#pragma unroll
+    for (int v4 = 0; v4 < kTopkWaves / 4; ++v4) {
+      const u32x4 w4 = reinterpret_cast<const u32x4*>(s_wsum)[v4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) above += 4 * v4 + e > wave ? w4[e] : 0u;
     }
-    if (tid < 256) {
-      const int above = s_scan[tid] - c;
-      if (above < krem && krem <= s_scan[tid]) {
-        s_prefix = prefix | ((uint32_t)tid << shift);
-        s_krem = krem - above;
-      }
+    const uint32_t ge = sfx + above, gt = ge - c;
+    if (part == 0 && gt < (uint32_t)krem && (uint32_t)krem <= ge) {
+      s_sel[0] = prefix | ((uint32_t)bin << shift);
+      s_sel[1] = (uint32_t)krem - gt;
+      s_sel[2] = c;
     }
     __syncthreads();
-    prefix = s_prefix;
-    krem = s_krem;
-    mask |= 255u << shift;
-    __syncthreads();
+    prefix = s_sel[0];
+    krem = (int)s_sel[1];
+    eqc = s_sel[2];
   }
-  // prefix = the k-th largest key: take all keys > prefix and the first krem keys
-  // == prefix, in index order. Round w covers keys [1024 w, 1024 w + 1024); a
-  // wave's 64 consecutive keys are ranked with ballots, waves with LDS counts.
-  const int wave = tid >> 6, lane = tid & 63;
-  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  int gt_carry = 0, eq_carry = 0;  // selected-above and tied keys in earlier rounds
-  for (int w = 0; w < rounds; ++w) {
-    const int j = tid + w * kTopkThreads;
-    const uint32_t key = j < n ? key_at(j) : 0u;
-    const bool gt = j < n && key > prefix;
-    const bool eq = j < n && key == prefix;
-    const uint64_t bgt = __ballot(gt), beq = __ballot(eq);
-    const int buf = w & 1;
+
+  // prefix is the k-th largest key. Output order = index order: waves, then
+  // sub-blocks, then lanes, then e. Outputs of up to 16384 indices are staged
+  // in LDS (the histogram space) and copied out coalesced.
+  const bool stage = k <= 256 * 64;
+  uint32_t* s_out = hist;
+  if (eqc == (uint32_t)krem) {
+    // every key >= prefix is taken
+    int g = 0;
+#pragma unroll
+    for (int u = 0; u < (S > 0 ? S : ns); ++u) {
+      const u32x4 x = SEGKV_TOPK_KEYS(u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g += __popcll(__ballot(x[e] >= prefix));
+    }
+    if (lane == 0) s_tot[wave][0] = g;
+    __syncthreads();
+    int gb = 0;
+    for (int v = 0; v < wave; ++v) gb += s_tot[v][0];
+#pragma unroll
+    for (int u = 0; u < (S > 0 ? S : ns); ++u) {
+      const u32x4 x = SEGKV_TOPK_KEYS(u);
+      uint64_t m[4];
+      int pos = gb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        m[e] = __ballot(x[e] >= prefix);
+        pos += lanes_below(m[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (x[e] >= prefix) {
+          const int j = base + kTopkSub * u + e;
+          if (stage) s_out[pos] = (uint32_t)j;
+          else idx_out[pos] = j;
+          ++pos;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gb += __popcll(m[e]);
+    }
+  } else {
+    // keys > prefix, then the first krem keys == prefix
+    int g = 0, q = 0;
+#pragma unroll
+    for (int u = 0; u < (S > 0 ? S : ns); ++u) {
+      const u32x4 x = SEGKV_TOPK_KEYS(u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        g += __popcll(__ballot(x[e] > prefix));
+        q += __popcll(__ballot(x[e] == prefix));
+      }
+    }
     if (lane == 0) {
-      wcnt[buf][wave][0] = __popcll(bgt);
-      wcnt[buf][wave][1] = __popcll(beq);
+      s_tot[wave][0] = g;
+      s_tot[wave][1] = q;
     }
     __syncthreads();
-    int gt_before = gt_carry + __popcll(bgt & lt_mask), eq_before = eq_carry + __popcll(beq & lt_mask);
-    int gt_round = 0, eq_round = 0;
-    for (int v = 0; v < kTopkThreads / 64; ++v) {
-      const int g = wcnt[buf][v][0], e = wcnt[buf][v][1];
-      if (v < wave) {
-        gt_before += g;
-        eq_before += e;
-      }
-      gt_round += g;
-      eq_round += e;
+    int gb = 0, qb = 0;
+    for (int v = 0; v < wave; ++v) {
+      gb += s_tot[v][0];
+      qb += s_tot[v][1];
     }
-    if (gt || (eq && eq_before < krem)) idx_out[gt_before + imin(eq_before, krem)] = j;
-    gt_carry += gt_round;
-    eq_carry += eq_round;
+#pragma unroll
+    for (int u = 0; u < (S > 0 ? S : ns); ++u) {
+      const u32x4 x = SEGKV_TOPK_KEYS(u);
+      uint64_t mg[4], mq[4];
+      int go = gb, qo = qb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mg[e] = __ballot(x[e] > prefix);
+        mq[e] = __ballot(x[e] == prefix);
+        go += lanes_below(mg[e]);
+        qo += lanes_below(mq[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool isg = x[e] > prefix, isq = x[e] == prefix;
+        if (isg || (isq && qo < krem)) {
+          const int pos = go + imin(qo, krem), j = base + kTopkSub * u + e;
+          if (stage) s_out[pos] = (uint32_t)j;
+          else idx_out[pos] = j;
+        }
+        go += isg ? 1 : 0;
+        qo += isq ? 1 : 0;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gb += __popcll(mg[e]);
+        qb += __popcll(mq[e]);
+      }
+    }
   }
+  if (stage) {
+    __syncthreads();
+    for (int x = tid; x < k; x += kTopkThreads) idx_out[x] = (int32_t)s_out[x];
+  }
+#undef SEGKV_TOPK_KEYS
 }
+#pragma clang diagnostic pop
 
 int32_t launch_topk(const float* scores, int32_t* idx, int n, int k, hipStream_t s) {
   if (k <= 0) return SEGKV_OK;
-  topk_kernel<<<1, kTopkThreads, 0, s>>>(scores, idx, n, k);
+  if (n > (1 << 30)) return fail(SEGKV_ERR_UNSUPPORTED, "top-k vectors are limited to 2^30 keys");
+  const int ns = cdiv(n, kTopkWaves * kTopkSub);  // sub-blocks per wave
+  const dim3 g(1), b(kTopkThreads);
+#define SEGKV_TOPK(SV) topk_kernel<SV><<<g, b, 0, s>>>(scores, idx, n, k, ns)
+  switch (ns <= kTopkMaxRegSub ? ns : 0) {
+    case 1: SEGKV_TOPK(1); break;
+    case 2: SEGKV_TOPK(2); break;
+    case 3: SEGKV_TOPK(3); break;
+    case 4: SEGKV_TOPK(4); break;
+    case 5: SEGKV_TOPK(5); break;
+    case 6: SEGKV_TOPK(6); break;
+    case 7: SEGKV_TOPK(7); break;
+    case 8: SEGKV_TOPK(8); break;
+    case 9: SEGKV_TOPK(9); break;
+    case 10: SEGKV_TOPK(10); break;
+    case 11: SEGKV_TOPK(11); break;
+    case 12: SEGKV_TOPK(12); break;
+    case 13: SEGKV_TOPK(13); break;
+    case 14: SEGKV_TOPK(14); break;
+    case 15: SEGKV_TOPK(15); break;
+    default: SEGKV_TOPK(0); break;
+  }
+#undef SEGKV_TOPK
   SEGKV_LAUNCH_CHECK();
   return SEGKV_OK;
 }
@@ -341,8 +504,8 @@ extern "C" int32_t token_importance_topk(const segkv_dims* dims, const segkv_met
   if (n_last <= 0) return fail(SEGKV_ERR_INVALID_ARG, "n_last must be > 0");
   const int G = dims->num_q_heads / dims->num_kv_heads;
   if (dims->num_kv_heads > kImpMaxHeads) return fail(SEGKV_ERR_UNSUPPORTED, "num_kv_heads must be <= 64");
-  if ((int64_t)dims->num_q_heads * n_last > 4096)
-    return fail(SEGKV_ERR_UNSUPPORTED, "num_q_heads * n_last must be <= 4096");
+  if ((int64_t)dims->num_q_heads * 32 * cdiv(n_last, 32) > kImpMaxLse)
+    return fail(SEGKV_ERR_UNSUPPORTED, "num_q_heads * (n_last rounded up to 32) must be <= 4096");
   if (!(softmax_scale > 0.f)) return fail(SEGKV_ERR_INVALID_ARG, "softmax_scale must be > 0");
   if (pool_pages <= 0) return fail(SEGKV_ERR_INVALID_ARG, "pool_pages must be > 0");
   if (!aligned16(q) || !aligned16(k_pool)) return fail(SEGKV_ERR_ALIGNMENT, "q and k_pool must be 16-byte aligned");

@@ -56,6 +56,7 @@ struct PagesArgs {
   char* plan;
   int R, Hkv, G;
   int chunk_tiles;
+  int n_items;  // launch slots of the attention kernel (a multiple of 8)
   PlanLayout L;
 };
 
@@ -87,13 +88,13 @@ __device__ PairInfo pair_info(const PagesArgs& a, int k) {
 // itself, so it does not wait for the planning block.
 __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fill_blocks_per_pair) {
   __shared__ int s[kScanThreads];
-  __shared__ int bins[1024];
+  __shared__ int pair_maxc[kMaxPairs];  // most chunks of any m-tile of the pair
+  __shared__ int pair_ib[kMaxPairs];    // first group-major item position of the pair
   __shared__ PairInfo info[kMaxPairs];
   __shared__ int req_off[kMaxPairs + 1];
   __shared__ int mt_tiles[kMaxMTiles];
   __shared__ int mt_chunks[kMaxMTiles];
   __shared__ int red[2][kScanThreads / 64];
-  __shared__ int n_items_s;
   const int tid = threadIdx.x;
   const int n_pairs = a.R * a.Hkv;
 
@@ -239,41 +240,42 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
       },
       s);
 
-  // items bucketed by size (1024 size classes, largest first)
-  for (int b = tid; b < 1024; b += blockDim.x) bins[b] = 0;
-  __syncthreads();
-  // size classes: 1024 * (size - 1) / S fits in 32 bits because S <= 2^18 (contexts <= 2^24 tokens)
-  auto size_bin = [&](int sz) { return 1023 - ((sz - 1) * 1024) / S; };
-  for (int i = tid; i < n_mt; i += blockDim.x) {
-    const int nt = mt_tiles[i], nc = mt_chunks[i];
-    for (int c = 0; c < nc; ++c) atomicAdd(&bins[size_bin(chunk_tile_lo(nt, nc, c + 1) - chunk_tile_lo(nt, nc, c))], 1);
+  // items in XCD-aware order (see xcd_slot): group-major position of item
+  // (m-tile j of pair k, chunk c) = pair_ib[k] + c * nj_k + j
+  for (int k = tid; k < n_pairs; k += kScanThreads) {
+    const int r = k / a.Hkv, h = k % a.Hkv;
+    const int nj = (req_off[r + 1] - req_off[r]) / a.Hkv, i0 = req_off[r] + h * nj;
+    int mc = 0;
+    for (int j = 0; j < nj; ++j) mc = imax(mc, mt_chunks[i0 + j]);
+    pair_maxc[k] = mc;
   }
   __syncthreads();
-  {  // bin counts -> start cursors (largest size class first), block-parallel
-    const int c = bins[tid];
-    s[tid] = c;
-    __syncthreads();
-    for (int off = 1; off < kScanThreads; off <<= 1) {
-      const int t = tid >= off ? s[tid - off] : 0;
-      __syncthreads();
-      s[tid] += t;
-      __syncthreads();
+  const int n_pos = block_exclusive_scan(
+      n_pairs, [&](int k) {
+        const int r = k / a.Hkv;
+        return pair_maxc[k] * ((req_off[r + 1] - req_off[r]) / a.Hkv);
+      },
+      [&](int k, int p) { pair_ib[k] = p; }, s);
+  const int q8 = a.n_items / kXcds;
+  for (int i = tid; i < n_mt; i += kScanThreads) {
+    int lo = 0, hi = a.R - 1;  // request: last r with req_off[r] <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (req_off[mid] <= i) lo = mid; else hi = mid - 1;
     }
-    bins[tid] = s[tid] - c;
-    if (tid == kScanThreads - 1) n_items_s = s[tid];
-  }
-  __syncthreads();
-  for (int i = tid; i < n_mt; i += blockDim.x) {
-    const int nt = mt_tiles[i], nc = mt_chunks[i];
-    for (int c = 0; c < nc; ++c) {
-      const int slot = atomicAdd(&bins[size_bin(chunk_tile_lo(nt, nc, c + 1) - chunk_tile_lo(nt, nc, c))], 1);
-      items[slot] = Item{i, c};
+    const int r = lo;
+    const int nj = (req_off[r + 1] - req_off[r]) / a.Hkv;
+    const int h = (i - req_off[r]) / nj, j = (i - req_off[r]) % nj, k = r * a.Hkv + h;
+    for (int c = 0; c < pair_maxc[k]; ++c) {
+      const int p = pair_ib[k] + c * nj + j;
+      if (p < a.n_items) items[xcd_slot(p, q8)] = c < mt_chunks[i] ? Item{i, c} : Item{-1, 0};
     }
   }
+  for (int p = n_pos + tid; p < a.n_items; p += kScanThreads) items[xcd_slot(p, q8)] = Item{-1, 0};
   if (tid == 0) {
     PlanHeader h;
     h.n_mtiles = n_mt;
-    h.n_items = n_items_s;
+    h.n_items = a.n_items;
     h.n_split = n_split;
     h.chunk_tiles = S;
     h.n_partials = n_partials;
@@ -393,6 +395,7 @@ extern "C" int32_t segkv_build_pages(const segkv_dims* dims, const segkv_meta* m
   a.Hkv = dims->num_kv_heads;
   a.G = dims->num_q_heads / dims->num_kv_heads;
   a.chunk_tiles = hp.chunk_tiles;
+  a.n_items = hp.n_items;
   a.L = plan_layout(a.R * a.Hkv, a.R, hp.n_mtiles, hp.n_items, hp.n_split);
   hipStream_t s = static_cast<hipStream_t>(stream);
   int max_pages = 1;

@@ -169,8 +169,18 @@ struct MTile {
 };
 
 struct Item {
-  int32_t mtile, chunk;
+  int32_t mtile, chunk;  // mtile < 0: empty slot, the work-group exits
 };
+
+// XCD-aware item order. Work-groups are dispatched round-robin over the 8 XCDs
+// of the chip, each with its own L2, so launch slot b runs on XCD b % 8. Items
+// are first listed group-major: per (request, kv head) pair, chunk c of every
+// m-tile of the pair, then chunk c + 1, ... (holes where an m-tile has fewer
+// chunks). The m-tiles of a group read the same key pages. That list is cut
+// into 8 equal runs of q8 positions, and run x goes to the slots of XCD x in
+// order, so a group's items run side by side on one XCD and share its L2.
+constexpr int kXcds = 8;
+SEGKV_HD int xcd_slot(int p, int q8) { return kXcds * (p % q8) + p / q8; }
 
 struct PlanLayout {
   size_t move_off_off;   // int32 [R*Hkv + 1]: first move of each (r, h)

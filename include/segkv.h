@@ -204,10 +204,12 @@ int32_t token_importance_topk(const segkv_dims* dims, const segkv_meta* meta_hos
                               int32_t* topk_idx_dev, void* stream);
 
 /*
- * Top-k of one non-negative fp32 score vector (scores: device [n]): the k
- * indices with the largest scores, ties to the lower index, ascending.
- * Same selection rule as token_importance_topk. NaN and negative scores are
- * not supported (SEGKV results unspecified).
+ * Top-k of one fp32 score vector (scores: device [n], n <= 2^30): the k
+ * indices with the largest scores, ties to the lower index, ascending; -0 and
+ * +0 are equal. Same selection rule as token_importance_topk. NaN scores are
+ * not supported (the selection is then unspecified). One 1024-thread
+ * work-group per vector; vectors of up to 61440 scores stay in registers,
+ * longer ones are re-read from memory on each of the five passes.
  */
 int32_t segkv_topk_select(const float* scores_dev, int32_t n, int32_t k, int32_t* idx_dev, void* stream);
 

@@ -83,7 +83,8 @@ def test_mixed_classes_multi_request():
 
 
 @pytest.mark.parametrize("n,k,levels", [(1000, 100, 7), (33280, 8320, 50), (4096, 4096, 3), (5, 1, 1),
-                                        (70000, 1, 0), (2049, 2048, 2)])
+                                        (70000, 1, 0), (2049, 2048, 2), (4097, 100, 0), (61440, 30000, 0),
+                                        (61441, 5, 0), (70000, 35000, 1000), (36864, 36863, 1)])
 def test_topk_select_ties(n, k, levels):
     print(f"case topk n={n} k={k} levels={levels}", flush=True)
     x = workloads.uniform_f32(seed=n + k, n=n, levels=levels)
@@ -93,3 +94,18 @@ def test_topk_select_ties(n, k, levels):
     torch.cuda.synchronize()
     ref = sorted(sorted(range(n), key=lambda j: (-float(x[j]), j))[:k])
     assert idx.cpu().numpy().tolist() == ref
+
+
+def test_topk_select_signed_scores():
+    """Negative scores and signed zeros: -0 and +0 tie, ties go to the lower index."""
+    n, k = 9000, 4500
+    print(f"case topk signed n={n} k={k}", flush=True)
+    x = workloads.uniform_f32(seed=77, n=n, lo=-1.0, hi=1.0)
+    x[::7] = np.float32(0.0)
+    x[3::7] = np.float32(-0.0)
+    x[5::11] = np.float32(-1e-30)
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    from head_aware_paged_amd import segkv_topk_select
+    segkv_topk_select(torch.from_numpy(x).cuda(), n, k, idx)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), oracle.topk_select(x, k))
