@@ -49,7 +49,8 @@ class Meta(ctypes.Structure):
 class Sizes(ctypes.Structure):
     _fields_ = [("table_entries", ctypes.c_int64), ("move_entries", ctypes.c_int64),
                 ("total_q_rows", ctypes.c_int64), ("total_keys", ctypes.c_int64),
-                ("plan_bytes", ctypes.c_size_t), ("attn_workspace_bytes", ctypes.c_size_t)]
+                ("plan_bytes", ctypes.c_size_t), ("attn_workspace_bytes", ctypes.c_size_t),
+                ("importance_workspace_bytes", ctypes.c_size_t)]
 
 
 _lib = None
@@ -73,7 +74,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "segkv_visible_spans": ([P, P, P, P, P, P], I32),
         "rope_relocate": ([P, P, P, P, I64, I64, P, P, P, I32, I32, I32, F64, P], I32),
         "segpaged_attn_prefill": ([P, P, P, P, P, I64, P, P, P, SZ, F32, P, P, P, SZ, P], I32),
-        "token_importance_topk": ([P, P, P, P, P, P, I64, P, P, P, P, F32, I32, P, P, P, P], I32),
+        "token_importance_topk": ([P, P, P, P, P, P, I64, P, P, P, P, SZ, P, F32, I32, P, P, P, P, SZ, P], I32),
         "segkv_topk_select": ([P, I32, I32, P, P], I32),
         "sparse_ffn_workspace_size": ([I32, I32], SZ),
         "sparse_ffn_swiglu": ([P, I32, I32, I32, P, I32, P, P, P, P, SZ, P], I32),
@@ -191,15 +192,17 @@ def segpaged_attn_prefill(d: Dims, meta: HostMeta, q, k_pool, v_pool, page_ids, 
 
 
 def token_importance_topk(d: Dims, meta: HostMeta, dmeta: DeviceMeta, cu_q, q, k_pool, page_indptr, page_ids,
-                          page_pos, lse, softmax_scale: float, n_last: int, k: Optional[Sequence[int]],
-                          importance, topk_idx=None, stream=None):
+                          page_pos, plan, lse, softmax_scale: float, n_last: int, k: Optional[Sequence[int]],
+                          importance, topk_idx=None, workspace=None, stream=None):
     lib = load()
     ms, dm = meta.struct(), dmeta.struct()
     k_arr = None if k is None else np.ascontiguousarray(k, np.int32)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("token_importance_topk", lib.token_importance_topk(
         ctypes.byref(d), ctypes.byref(ms), ctypes.byref(dm), _ptr(cu_q), _ptr(q), _ptr(k_pool), k_pool.shape[0],
-        _ptr(page_indptr), _ptr(page_ids), _ptr(page_pos), _ptr(lse), float(softmax_scale), int(n_last),
-        _ptr(k_arr), _ptr(importance), _ptr(topk_idx), _stream(stream)))
+        _ptr(page_indptr), _ptr(page_ids), _ptr(page_pos), _ptr(plan), plan.numel() * plan.element_size(),
+        _ptr(lse), float(softmax_scale), int(n_last),
+        _ptr(k_arr), _ptr(importance), _ptr(topk_idx), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def segkv_topk_select(scores, n: int, k: int, idx, stream=None):

@@ -177,6 +177,7 @@ int32_t compute_host_plan(const segkv_dims* d, const segkv_meta* m, HostPlan* ou
       const PageRuns pr = head_page_runs(v);
       const int cnt = runs_count(pr);
       p.table_entries += cnt;
+      p.n_imp_items += runs_count(block_runs(pr));
       p.move_entries += runs_rank(pr, v.bq / kPage);
       if (h == 0) {
         p.total_q_rows += v.Lq;
@@ -216,7 +217,7 @@ int32_t compute_host_plan(const segkv_dims* d, const segkv_meta* m, HostPlan* ou
   }
   REQUIRE(positions < (int64_t)1 << 30, SEGKV_ERR_UNSUPPORTED, "too many attention work items");
   p.n_items = kXcds * (int)((positions + kXcds - 1) / kXcds);
-  const PlanLayout L = plan_layout(R * Hkv, R, p.n_mtiles, p.n_items, p.n_split);
+  const PlanLayout L = plan_layout(R * Hkv, R, p.n_mtiles, p.n_items, p.n_split, p.n_imp_items);
   p.plan_bytes = L.total;
   p.workspace_bytes = (size_t)p.n_partials * partial_slot_bytes(d->head_dim);
   *out = p;
@@ -254,5 +255,6 @@ extern "C" int32_t segkv_plan_sizes(const segkv_dims* dims, const segkv_meta* me
   sizes->total_keys = p.total_keys;
   sizes->plan_bytes = p.plan_bytes;
   sizes->attn_workspace_bytes = p.workspace_bytes;
+  sizes->importance_workspace_bytes = importance_workspace_bytes(*dims, p.total_keys);
   return SEGKV_OK;
 }

@@ -33,176 +33,167 @@ struct ImpArgs {
   const int32_t* page_indptr;
   const int32_t* page_ids;
   const float* lse;
+  const char* plan;     // attention plan of the layout (its importance item list)
+  PlanLayout L;
+  float* partial;       // workspace [Hkv][total_keys]: per-kv-head importance
   float* importance;
+  int64_t total_keys;
   float scale_log2;
   int R, Hq, Hkv, G, n_last;
 };
 
-constexpr int kImpMaxHeads = 64;  // kv heads per request (one 64-bit wave vote)
-constexpr int kImpMaxLse = 4096;  // Hq * (n_last rounded up to 32) values staged in LDS
+constexpr int kImpMaxLse = 4096;  // Hq * (n_last rounded up to 32) values (bounds one head's G * NP)
 
-// One work-group per 64-key block of one request. Its work is a list of
-// (kv head with a page at this block, 32-row block) units; wave w takes the
-// contiguous unit range [U w / 4, U (w + 1) / 4), so blocks that several
-// heads see spread those heads over the waves. Those blocks sit at the end of
-// the context (the local windows), so work-groups are numbered from the last
-// block backwards and the heavy ones start first. K and Q fragments go from
-// memory straight into MFMA operand registers; the next unit's Q is in flight
-// while the current one computes. Units whose 32 rows see all 64 keys skip
-// every mask.
+// One work-group per importance item of the plan: a 64-key block that one
+// (request, kv head) table touches. It computes that head's share of the
+// block's importance as (32-row block of one of its G query heads) units,
+// wave w taking units [U w / 4, U (w + 1) / 4), and writes the block's 64
+// partial sums; a second kernel adds, key by key, the partials of the heads
+// whose tables touch the key's block, in head order. Each score is thus summed
+// in a fixed order with no float atomics. K and Q fragments go from memory
+// straight into MFMA operand registers; the next unit's Q is in flight while
+// the current one computes; units whose 32 rows see all 64 keys skip every
+// mask.
 template <int D>
-__global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
+__global__ __launch_bounds__(kImpThreads, 3) void importance_kernel(ImpArgs a) {
   constexpr int KS = D / 16;
-  __shared__ float s_lse[kImpMaxLse];
-  __shared__ int s_pid[kImpMaxHeads][kTilePages];  // page of each head's table at this key block, -1 if none
-  __shared__ int s_cls[kImpMaxHeads], s_W[kImpMaxHeads];
+  constexpr int KCH = D / 8;            // 16-byte chunks per key row
+  constexpr int kStride = D + 8;        // padded LDS row (elements)
+  constexpr int KLOADS = kTileKeys * KCH / kImpThreads;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kTileKeys * kStride];
+  __shared__ __attribute__((aligned(16))) float s_lse[kImpMaxLse];
+  __shared__ int s_pid[kTilePages];  // this head's page at each page of the key block, -1 if none
   __shared__ float colsum[kImpWaves][kTileKeys];
 
-  const int r = blockIdx.y;
+  const ImpItem item = reinterpret_cast<const ImpItem*>(a.plan + a.L.imp_items_off)[blockIdx.x];
+  if (item.pair < 0 || item.pair >= a.R * a.Hkv || item.block < 0) return;  // not a plan of this layout
+  const int r = item.pair / a.Hkv, hh = item.pair % a.Hkv;
   const int sq = a.m.seg_indptr[r + 1] - 1;
   const int bq = a.m.seg_start[sq], Lq = a.m.seg_len[sq], Lk = bq + Lq;
-  const int kb0 = (gridDim.x - 1 - blockIdx.x) * kTileKeys;
+  const int kb0 = item.block * kTileKeys;
   if (kb0 >= Lk) return;
-  int off = 0;  // output offset of request r: sum of earlier context lengths
-  for (int rr = 0; rr < r; ++rr) {
-    const int s2 = a.m.seg_indptr[rr + 1] - 1;
-    off += a.m.seg_start[s2] + a.m.seg_len[s2];
-  }
   const int n = imin(a.n_last, Lq);
   const int nb_head = cdiv(n, 32);  // 32-row blocks per query head
   const int NP = 32 * nb_head;      // staged rows per query head (the last row repeated)
-  const int R8 = a.G * nb_head;     // units per kv head
+  const int U = a.G * nb_head;      // units of this kv head
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lrow = lane & 31, lg = lane >> 5;
   const int q_base = a.cu_q[r] + Lq - n;  // first of the last n query rows
   const int pos_base = Lk - n;            // its position
+  const int u_lo = U * wave / kImpWaves, u_hi = U * (wave + 1) / kImpWaves;
 
-  // ---- everything per head that does not depend on the rows, loaded once ----
-  for (int x = tid; x < a.Hkv * kTilePages; x += kImpThreads) {
-    const int h = x / kTilePages, pp = x % kTilePages;
-    const HeadView v = head_view_dev(a.m, a.Hkv, r, h);
+  // the wave's first Q fragment (A operand: Q row tb + lrow of query head hg)
+  // is requested before the page lookups, so its latency overlaps them
+  bf16x8 qa[KS];
+  auto q_load = [&](bf16x8* dst, int uu) {
+    const int hg = uu / nb_head, tb = (uu % nb_head) * 32;
+    const uint16_t* qp = a.q + ((size_t)(q_base + imin(tb + lrow, n - 1)) * a.Hq + hh * a.G + hg) * D + 8 * lg;
+#pragma unroll
+    for (int k8 = 0; k8 < KS; ++k8) dst[k8] = *reinterpret_cast<const bf16x8*>(qp + 16 * k8);
+  };
+  if (u_lo < u_hi) q_load(qa, u_lo);
+
+  const HeadView v = head_view_dev(a.m, a.Hkv, r, hh);
+  if (tid < kTilePages) {
     const PageRuns pr = head_page_runs(v);
-    const int page = kb0 / kPage + pp;
+    const int page = kb0 / kPage + tid;
     const int rk = runs_rank(pr, page);
     int pid = -1;
     if (runs_rank(pr, page + 1) - rk == 1) {
-      pid = a.page_ids[a.page_indptr[r * a.Hkv + h] + rk];
+      pid = a.page_ids[a.page_indptr[r * a.Hkv + hh] + rk];
       if (pid < 0 || pid >= a.pool_pages) pid = -1;
     }
-    s_pid[h][pp] = pid;
-    if (pp == 0) {
-      s_cls[h] = v.cls;
-      s_W[h] = v.W;
+    s_pid[tid] = pid;
+  }
+  // log2-scaled LSE of the last n rows of this head's G query heads, [g][t]
+  // with t < NP (rows past n repeat row n - 1); loads first, then stores
+  for (int x0 = 0; x0 < a.G * NP; x0 += 4 * kImpThreads) {
+    float lv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = x0 + u * kImpThreads + tid;
+      lv[u] = x < a.G * NP ? a.lse[(size_t)(q_base + imin(x % NP, n - 1)) * a.Hq + hh * a.G + x / NP] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = x0 + u * kImpThreads + tid;
+      if (x < a.G * NP) s_lse[x] = lv[u] * kLog2e;
     }
   }
-  // log2-scaled LSE of the last n rows, [g][t] with t < NP (rows past n repeat
-  // row n - 1); all loads of a thread are issued before its stores
-  for (int x0 = 0; x0 < a.Hq * NP; x0 += 8 * kImpThreads) {
-    float v[8];
+  __syncthreads();
+  // K tile -> LDS (rows of missing pages are zero)
+  {
+    u32x4 kr[KLOADS];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int x = x0 + u * kImpThreads + tid;
-      v[u] = x < a.Hq * NP ? a.lse[(size_t)(q_base + imin(x % NP, n - 1)) * a.Hq + x / NP] : 0.f;
+    for (int u = 0; u < KLOADS; ++u) {
+      const int qd = tid + u * kImpThreads, key = qd / KCH, c = qd % KCH;
+      const int pid = s_pid[key >> 4];
+      kr[u] = pid >= 0 ? *reinterpret_cast<const u32x4*>(a.k_pool + ((size_t)pid * kPage + (key & 15)) * D + 8 * c)
+                       : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int x = x0 + u * kImpThreads + tid;
-      if (x < a.Hq * NP) s_lse[x] = v[u] * kLog2e;
+    for (int u = 0; u < KLOADS; ++u) {
+      const int qd = tid + u * kImpThreads;
+      *reinterpret_cast<u32x4*>(&ks[(qd / KCH) * kStride + 8 * (qd % KCH)]) = kr[u];
     }
   }
   __syncthreads();
 
-  // heads with a page at this key block (the same vote in every wave)
-  const bool on = lane < a.Hkv && (s_pid[lane][0] >= 0 || s_pid[lane][1] >= 0 || s_pid[lane][2] >= 0 ||
-                                   s_pid[lane][3] >= 0);
-  const uint64_t act = __ballot(on);
-  const int U = __popcll(act) * R8;
-  const int u_lo = (int)((int64_t)U * wave / kImpWaves), u_hi = (int)((int64_t)U * (wave + 1) / kImpWaves);
+  const int cls = v.cls, W = v.W;
+  const bool pages_full = s_pid[0] >= 0 && s_pid[1] >= 0 && s_pid[2] >= 0 && s_pid[3] >= 0;
+  const int pa = s_pid[lrow >> 4], pb = s_pid[2 + (lrow >> 4)];
+  const int j0 = pa < 0 ? INT_MAX : kb0 + lrow;
+  const int j1 = pb < 0 ? INT_MAX : kb0 + 32 + lrow;
 
   float acc0 = 0.f, acc1 = 0.f;  // keys lrow and 32 + lrow, this lane's rows
-  bf16x8 kf[2][KS], qa[KS], qb[KS];
-  uint64_t rest = act;
-  for (int hi = 0; hi < u_lo / R8; ++hi) rest &= rest - 1;  // drop heads before the wave's first unit
-  int u = u_lo;
-  while (u < u_hi) {
-    const int hh = __builtin_ctzll(rest);
-    rest &= rest - 1;
-    const int u_end = imin(u_hi, (u / R8 + 1) * R8);
-    // B operand: key 32 kb + lrow, dims 16 ks + 8 lg .. + 8
+  // unit uu with Q in qa; once its MFMAs have read qa, the next unit's Q is
+  // requested into qa, so that load overlaps this unit's exponentials
+  auto unit = [&](int uu) {
+    f32x16 s0, s1;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = 32 * kb + lrow;
-      const int pid = s_pid[hh][key >> 4];
-      const uint16_t* kp = a.k_pool + ((size_t)imax(pid, 0) * kPage + (key & 15)) * D + 8 * lg;
+    for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = pid >= 0 ? *reinterpret_cast<const bf16x8*>(kp + 16 * ks) : bf16x8{};
+    for (int k8 = 0; k8 < KS; ++k8) {  // B operand: key 32 kb + lrow, dims 16 k8 + 8 lg .. + 8
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(&ks[lrow * kStride + 16 * k8 + 8 * lg]);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(&ks[(32 + lrow) * kStride + 16 * k8 + 8 * lg]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[k8], k0, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[k8], k1, s1, 0, 0, 0);
     }
-    const int cls = s_cls[hh], W = s_W[hh];
-    const bool pages_full = s_pid[hh][0] >= 0 && s_pid[hh][1] >= 0 && s_pid[hh][2] >= 0 && s_pid[hh][3] >= 0;
-    const int pa = s_pid[hh][lrow >> 4], pb = s_pid[hh][2 + (lrow >> 4)];
-    const int j0 = pa < 0 ? INT_MAX : kb0 + lrow;
-    const int j1 = pb < 0 ? INT_MAX : kb0 + 32 + lrow;
-
-    auto q_load = [&](bf16x8* dst, int uu) {  // A operand: Q row tb + lrow of head hg
-      const int rb = uu % R8, hg = rb / nb_head, tb = (rb % nb_head) * 32;
-      const uint16_t* qp = a.q + ((size_t)(q_base + imin(tb + lrow, n - 1)) * a.Hq + hh * a.G + hg) * D + 8 * lg;
+    if (uu + 1 < u_hi) q_load(qa, uu + 1);
+    // lane holds keys (j0, j1) for rows t = tb + 8(i/4) + 4 lg + i%4 of query head hg
+    const int hg = uu / nb_head, tb = (uu % nb_head) * 32;
+    const float* lse_h = &s_lse[hg * NP + tb + 4 * lg];
+    f32x4 l2[4];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) dst[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
-    };
-    auto unit = [&](const bf16x8* qf, int uu) {
-      f32x16 s0, s1;
+    for (int c = 0; c < 4; ++c) l2[c] = *reinterpret_cast<const f32x4*>(lse_h + 8 * c);
+    const int pos0 = pos_base + tb;  // position of row tb
+    const bool full = pages_full && tb + 32 <= n && kb0 + kTileKeys - 1 <= pos0 &&
+                      (cls != kClassLocal || kb0 >= local_lo(pos0 + 31, bq, W));
+    float p0 = 0.f, p1 = 0.f;
+    if (full) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[0][ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[1][ks], s1, 0, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        p0 += __builtin_amdgcn_exp2f(fmaf(s0[i], a.scale_log2, -l2[i >> 2][i & 3]));
+        p1 += __builtin_amdgcn_exp2f(fmaf(s1[i], a.scale_log2, -l2[i >> 2][i & 3]));
       }
-      // lane holds keys (j0, j1) for rows t = tb + 8(i/4) + 4 lg + i%4 of query head hg
-      const int rb = uu % R8, hg = rb / nb_head, tb = (rb % nb_head) * 32;
-      const float* lse_h = &s_lse[(hh * a.G + hg) * NP + tb + 4 * lg];
-      f32x4 l2[4];
+    } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) l2[c] = *reinterpret_cast<const f32x4*>(lse_h + 8 * c);
-      const int pos0 = pos_base + tb;  // position of row tb
-      const bool full = pages_full && tb + 32 <= n && kb0 + kTileKeys - 1 <= pos0 &&
-                        (cls != kClassLocal || kb0 >= local_lo(pos0 + 31, bq, W));
-      float p0 = 0.f, p1 = 0.f;
-      if (full) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p0 += __builtin_amdgcn_exp2f(fmaf(s0[i], a.scale_log2, -l2[i >> 2][i & 3]));
-          p1 += __builtin_amdgcn_exp2f(fmaf(s1[i], a.scale_log2, -l2[i >> 2][i & 3]));
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int t = tb + 8 * (i >> 2) + 4 * lg + (i & 3);
-          const bool row_ok = t < n;
-          const int pos = pos_base + t;
-          const int lo = cls == kClassLocal ? local_lo(pos, bq, W) : 0;
-          const float e0 = __builtin_amdgcn_exp2f(fmaf(s0[i], a.scale_log2, -l2[i >> 2][i & 3]));
-          const float e1 = __builtin_amdgcn_exp2f(fmaf(s1[i], a.scale_log2, -l2[i >> 2][i & 3]));
-          p0 += (row_ok && j0 <= pos && j0 >= lo) ? e0 : 0.f;
-          p1 += (row_ok && j1 <= pos && j1 >= lo) ? e1 : 0.f;
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int t = tb + 8 * (i >> 2) + 4 * lg + (i & 3);
+        const bool row_ok = t < n;
+        const int pos = pos_base + t;
+        const int lo = cls == kClassLocal ? local_lo(pos, bq, W) : 0;
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(s0[i], a.scale_log2, -l2[i >> 2][i & 3]));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(s1[i], a.scale_log2, -l2[i >> 2][i & 3]));
+        p0 += (row_ok && j0 <= pos && j0 >= lo) ? e0 : 0.f;
+        p1 += (row_ok && j1 <= pos && j1 >= lo) ? e1 : 0.f;
       }
-      acc0 += p0;
-      acc1 += p1;
-    };
-
-    // two units per trip, Q buffers alternating without copies; the prefetches
-    // are unconditional (clamped to the last unit) so every wait before an
-    // MFMA can leave the other buffer's loads in flight
-    q_load(qa, u);
-    for (; u < u_end; u += 2) {
-      q_load(qb, imin(u + 1, u_end - 1));
-      unit(qa, u);
-      q_load(qa, imin(u + 2, u_end - 1));
-      if (u + 1 < u_end) unit(qb, u + 1);
     }
-    u = u_end;
-  }
+    acc0 += p0;
+    acc1 += p1;
+  };
+
+  for (int u = u_lo; u < u_hi; ++u) unit(u);
   // lanes lg = 0 / 1 hold different rows of the same keys; then waves in order
   acc0 += __shfl_xor(acc0, 32);
   acc1 += __shfl_xor(acc1, 32);
@@ -211,13 +202,48 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
     colsum[wave][32 + lrow] = acc1;
   }
   __syncthreads();
-  if (tid < kTileKeys) {
-    const int j = kb0 + tid;
+  if (tid < kTileKeys && kb0 + tid < Lk) {
+    int off = 0;  // output offset of request r: sum of earlier context lengths
+    for (int rr = 0; rr < r; ++rr) {
+      const int s2 = a.m.seg_indptr[rr + 1] - 1;
+      off += a.m.seg_start[s2] + a.m.seg_len[s2];
+    }
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < kImpWaves; ++w) sum += colsum[w][tid];
-    if (j < Lk) a.importance[off + j] = sum;
+    a.partial[(size_t)hh * a.total_keys + off + kb0 + tid] = sum;
   }
+}
+
+constexpr int kImpMaxHeads = 256;  // kv heads whose block runs the reduction stages in LDS
+
+// importance[off + j] = sum, in head order, of the partials of the heads whose
+// tables touch key j's 64-key block (0 when none does). One work-group per
+// 256 keys of one request.
+__global__ __launch_bounds__(256) void importance_reduce_kernel(segkv_meta m, const float* __restrict__ partial,
+                                                                float* __restrict__ importance, int64_t total_keys,
+                                                                int Hkv) {
+  __shared__ PageRuns br[kImpMaxHeads];
+  const int r = blockIdx.y;
+  const int sq = m.seg_indptr[r + 1] - 1;
+  const int Lk = m.seg_start[sq] + m.seg_len[sq];
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if ((int)blockIdx.x * 256 >= Lk) return;
+  int off = 0;
+  for (int rr = 0; rr < r; ++rr) {
+    const int s2 = m.seg_indptr[rr + 1] - 1;
+    off += m.seg_start[s2] + m.seg_len[s2];
+  }
+  for (int h = threadIdx.x; h < Hkv; h += 256) br[h] = block_runs(head_page_runs(head_view_dev(m, Hkv, r, h)));
+  __syncthreads();
+  if (j >= Lk) return;
+  const int blk = j / kTileKeys;
+  float sum = 0.f;
+  for (int h = 0; h < Hkv; ++h) {
+    const PageRuns b = br[h];
+    if (runs_rank(b, blk + 1) - runs_rank(b, blk) == 1) sum += partial[(size_t)h * total_keys + off + j];
+  }
+  importance[off + j] = sum;
 }
 
 // ---- top-k: radix select on order-preserving integer keys ----
@@ -491,19 +517,24 @@ extern "C" int32_t token_importance_topk(const segkv_dims* dims, const segkv_met
                                          const segkv_meta* meta_dev, const int32_t* cu_q_dev, const void* q,
                                          const void* k_pool, int64_t pool_pages, const int32_t* page_indptr_dev,
                                          const int32_t* page_ids_dev, const int32_t* page_pos_dev,
+                                         const void* plan_dev, size_t plan_bytes,
                                          const float* lse_dev, float softmax_scale, int32_t n_last,
                                          const int32_t* k_host, float* importance_dev, int32_t* topk_idx_dev,
-                                         void* stream) {
+                                         void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
   HostPlan hp;
   int32_t st = compute_host_plan(dims, meta_host, &hp);
   if (st != SEGKV_OK) return st;
   if (!meta_dev || !meta_dev->seg_indptr || !cu_q_dev || !q || !k_pool || !page_indptr_dev || !page_ids_dev ||
-      !page_pos_dev || !lse_dev || !importance_dev)
+      !page_pos_dev || !plan_dev || !lse_dev || !importance_dev)
     return fail(SEGKV_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (plan_bytes < hp.plan_bytes) return fail(SEGKV_ERR_WORKSPACE, "plan smaller than plan_bytes from segkv_plan_sizes");
+  if (dims->num_kv_heads > kImpMaxHeads) return fail(SEGKV_ERR_UNSUPPORTED, "importance supports num_kv_heads <= 256");
   if (n_last <= 0) return fail(SEGKV_ERR_INVALID_ARG, "n_last must be > 0");
   const int G = dims->num_q_heads / dims->num_kv_heads;
-  if (dims->num_kv_heads > kImpMaxHeads) return fail(SEGKV_ERR_UNSUPPORTED, "num_kv_heads must be <= 64");
+  if (workspace == nullptr || workspace_bytes < importance_workspace_bytes(*dims, hp.total_keys))
+    return fail(SEGKV_ERR_WORKSPACE, "workspace smaller than importance_workspace_bytes from segkv_plan_sizes");
+  if (!aligned16(workspace)) return fail(SEGKV_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
   if ((int64_t)dims->num_q_heads * 32 * cdiv(n_last, 32) > kImpMaxLse)
     return fail(SEGKV_ERR_UNSUPPORTED, "num_q_heads * (n_last rounded up to 32) must be <= 4096");
   if (!(softmax_scale > 0.f)) return fail(SEGKV_ERR_INVALID_ARG, "softmax_scale must be > 0");
@@ -534,17 +565,26 @@ extern "C" int32_t token_importance_topk(const segkv_dims* dims, const segkv_met
   a.page_ids = page_ids_dev;
   a.lse = lse_dev;
   a.importance = importance_dev;
+  a.partial = static_cast<float*>(workspace);
+  a.plan = static_cast<const char*>(plan_dev);
+  a.L = plan_layout(R * dims->num_kv_heads, R, hp.n_mtiles, hp.n_items, hp.n_split, hp.n_imp_items);
+  a.total_keys = hp.total_keys;
   a.scale_log2 = softmax_scale * kLog2e;
   a.R = R;
   a.Hq = dims->num_q_heads;
   a.Hkv = dims->num_kv_heads;
   a.G = G;
   a.n_last = n_last;
-  dim3 grid(cdiv(max_lk, kTileKeys), R);
-  if (dims->head_dim == 128)
-    importance_kernel<128><<<grid, kImpThreads, 0, s>>>(a);
-  else
-    importance_kernel<64><<<grid, kImpThreads, 0, s>>>(a);
+  if (R > 65535) return fail(SEGKV_ERR_UNSUPPORTED, "importance supports at most 65535 requests");
+  if (hp.n_imp_items > 0) {
+    if (dims->head_dim == 128)
+      importance_kernel<128><<<hp.n_imp_items, kImpThreads, 0, s>>>(a);
+    else
+      importance_kernel<64><<<hp.n_imp_items, kImpThreads, 0, s>>>(a);
+    SEGKV_LAUNCH_CHECK();
+  }
+  importance_reduce_kernel<<<dim3(cdiv(max_lk, 256), R), 256, 0, s>>>(*meta_dev, a.partial, importance_dev,
+                                                                      hp.total_keys, a.Hkv);
   SEGKV_LAUNCH_CHECK();
   if (topk_idx_dev == nullptr) return SEGKV_OK;
   // one selection per request on the same stream (host knows every offset)

@@ -56,7 +56,8 @@ struct PagesArgs {
   char* plan;
   int R, Hkv, G;
   int chunk_tiles;
-  int n_items;  // launch slots of the attention kernel (a multiple of 8)
+  int n_items;      // launch slots of the attention kernel (a multiple of 8)
+  int n_imp_items;  // importance work items (64-key blocks of every table)
   PlanLayout L;
 };
 
@@ -272,6 +273,21 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
     }
   }
   for (int p = n_pos + tid; p < a.n_items; p += kScanThreads) items[xcd_slot(p, q8)] = Item{-1, 0};
+
+  // importance items: every 64-key block of every table, pair by pair
+  __syncthreads();  // pair_maxc is reused below
+  const int n_imp = block_exclusive_scan(
+      n_pairs, [&](int k) { return runs_count(block_runs(info[k].pr)); }, [&](int k, int p) { pair_maxc[k] = p; },
+      s);
+  ImpItem* imp_items = reinterpret_cast<ImpItem*>(a.plan + a.L.imp_items_off);
+  for (int x = tid; x < imin(n_imp, a.n_imp_items); x += kScanThreads) {
+    int lo = 0, hi = n_pairs - 1;  // pair: last k with base <= x
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pair_maxc[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    imp_items[x] = ImpItem{lo, runs_page(block_runs(info[lo].pr), x - pair_maxc[lo])};
+  }
   if (tid == 0) {
     PlanHeader h;
     h.n_mtiles = n_mt;
@@ -281,7 +297,7 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
     h.n_partials = n_partials;
     h.total_q_rows = a.cu_q[a.R];
     h.max_tiles = 0;
-    h.reserved = 0;
+    h.n_imp_items = n_imp;
     for (int q = 0; q < 8; ++q) h.pad[q] = 0;
     *hdr = h;
   }
@@ -396,7 +412,8 @@ extern "C" int32_t segkv_build_pages(const segkv_dims* dims, const segkv_meta* m
   a.G = dims->num_q_heads / dims->num_kv_heads;
   a.chunk_tiles = hp.chunk_tiles;
   a.n_items = hp.n_items;
-  a.L = plan_layout(a.R * a.Hkv, a.R, hp.n_mtiles, hp.n_items, hp.n_split);
+  a.n_imp_items = hp.n_imp_items;
+  a.L = plan_layout(a.R * a.Hkv, a.R, hp.n_mtiles, hp.n_items, hp.n_split, hp.n_imp_items);
   hipStream_t s = static_cast<hipStream_t>(stream);
   int max_pages = 1;
   for (int r = 0; r < a.R; ++r) {

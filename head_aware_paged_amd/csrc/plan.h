@@ -131,6 +131,44 @@ SEGKV_HD int runs_page(const PageRuns& pr, int e) {
   return page;
 }
 
+// The 64-key blocks (kTilePages pages) holding any page of a head's table, as
+// at most three ascending, disjoint block runs (slots written through constant
+// indices only).
+SEGKV_HD PageRuns block_runs(const PageRuns& pr) {
+  PageRuns b;
+  b.lo[1] = b.hi[1] = b.lo[2] = b.hi[2] = 0;
+  b.lo[0] = pr.lo[0] / kTilePages;
+  b.hi[0] = cdiv(pr.hi[0], kTilePages);
+  b.n = 1;
+  if (pr.n >= 2) {
+    const int lo = pr.lo[1] / kTilePages, hi = cdiv(pr.hi[1], kTilePages);
+    if (lo <= b.hi[0]) {
+      b.hi[0] = imax(b.hi[0], hi);
+    } else {
+      b.lo[1] = lo;
+      b.hi[1] = hi;
+      b.n = 2;
+    }
+  }
+  if (pr.n >= 3) {
+    const int lo = pr.lo[2] / kTilePages, hi = cdiv(pr.hi[2], kTilePages);
+    if (b.n == 1 && lo <= b.hi[0]) {
+      b.hi[0] = imax(b.hi[0], hi);
+    } else if (b.n == 1) {
+      b.lo[1] = lo;
+      b.hi[1] = hi;
+      b.n = 2;
+    } else if (lo <= b.hi[1]) {
+      b.hi[1] = imax(b.hi[1], hi);
+    } else {
+      b.lo[2] = lo;
+      b.hi[2] = hi;
+      b.n = 3;
+    }
+  }
+  return b;
+}
+
 // Table entry range [e0, e1) (relative to the (r, h) table) that query rows at
 // positions [i_lo, i_hi] can see. Rows are never empty: e1 > e0.
 SEGKV_HD void mtile_entries(const HeadView& v, const PageRuns& pr, int i_lo, int i_hi, int* e0, int* e1) {
@@ -152,7 +190,7 @@ SEGKV_HD int chunk_tile_lo(int n_tiles, int n_chunks, int c) {
 // ---- device plan layout (opaque to callers) ----
 struct PlanHeader {
   int32_t n_mtiles, n_items, n_split, chunk_tiles;
-  int32_t n_partials, total_q_rows, max_tiles, reserved;
+  int32_t n_partials, total_q_rows, max_tiles, n_imp_items;
   int32_t pad[8];
 };
 
@@ -182,22 +220,29 @@ struct Item {
 constexpr int kXcds = 8;
 SEGKV_HD int xcd_slot(int p, int q8) { return kXcds * (p % q8) + p / q8; }
 
+// Importance work item: one 64-key block of one (request, kv head) table.
+struct ImpItem {
+  int32_t pair, block;
+};
+
 struct PlanLayout {
   size_t move_off_off;   // int32 [R*Hkv + 1]: first move of each (r, h)
   size_t req_mt_off;     // int32 [R + 1]: first m-tile of each request
-  size_t mtiles_off, items_off, split_off, total;
+  size_t mtiles_off, items_off, split_off, imp_items_off, total;
 };
 
 SEGKV_HD size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-SEGKV_HD PlanLayout plan_layout(int n_pairs, int n_requests, int n_mtiles, int n_items, int n_split) {
+SEGKV_HD PlanLayout plan_layout(int n_pairs, int n_requests, int n_mtiles, int n_items, int n_split,
+                                int n_imp_items) {
   PlanLayout L;
   L.move_off_off = align256(sizeof(PlanHeader));
   L.req_mt_off = L.move_off_off + align256(sizeof(int32_t) * (size_t)(n_pairs + 1));
   L.mtiles_off = L.req_mt_off + align256(sizeof(int32_t) * (size_t)(n_requests + 1));
   L.items_off = L.mtiles_off + align256(sizeof(MTile) * (size_t)imax(n_mtiles, 1));
   L.split_off = L.items_off + align256(sizeof(Item) * (size_t)imax(n_items, 1));
-  L.total = L.split_off + align256(sizeof(int32_t) * (size_t)imax(n_split, 1));
+  L.imp_items_off = L.split_off + align256(sizeof(int32_t) * (size_t)imax(n_split, 1));
+  L.total = L.imp_items_off + align256(sizeof(ImpItem) * (size_t)imax(n_imp_items, 1));
   return L;
 }
 

@@ -45,6 +45,8 @@ class SegPagedLayer:
         self.plan = torch.zeros(self.sizes["plan_bytes"], dtype=torch.uint8, device=device)
         ws = self.sizes["attn_workspace_bytes"]
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device) if ws > 0 else None
+        self.imp_workspace = torch.empty(max(self.sizes["importance_workspace_bytes"], 16), dtype=torch.uint8,
+                                         device=device)
         self.scale = 1.0 / math.sqrt(head_dim)
 
     @property
@@ -88,8 +90,8 @@ class SegPagedLayer:
         if k is not None and topk_idx is None:
             topk_idx = torch.empty(max(1, int(sum(k))), dtype=torch.int32, device=self.device)
         token_importance_topk(self.dims, self.meta, self.dmeta, self.cu_q, q, k_pool, self.page_indptr,
-                              self.page_ids, self.page_pos, lse, self.scale, n_last, k, importance,
-                              topk_idx if k is not None else None, stream=stream)
+                              self.page_ids, self.page_pos, self.plan, lse, self.scale, n_last, k, importance,
+                              topk_idx if k is not None else None, workspace=self.imp_workspace, stream=stream)
         return importance, topk_idx
 
 

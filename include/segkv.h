@@ -91,6 +91,7 @@ typedef struct {
   int64_t total_keys;      /* sum of context lengths L_k (importance vector length) */
   size_t plan_bytes;       /* device plan buffer for segkv_build_pages / segpaged_attn_prefill */
   size_t attn_workspace_bytes;  /* device workspace for segpaged_attn_prefill */
+  size_t importance_workspace_bytes;  /* device workspace for token_importance_topk (Hkv x total_keys fp32) */
 } segkv_sizes;
 
 /* Status name ("SEGKV_OK", "SEGKV_ERR_INVALID_ARG", ...); static storage. */
@@ -194,14 +195,21 @@ int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_meta* meta_hos
  * importance, ties to the lower position, in ascending order; koff_r = sum of
  * k over earlier requests. k: host int32 [R], 0 <= k[r] <= L_k(r).
  * Other arguments as in segpaged_attn_prefill. topk_idx may be NULL to skip
- * selection.
+ * selection. plan: the plan written by segkv_build_pages for this layout (its
+ * importance work list: every 64-key block of every table). workspace:
+ * device, 16-byte aligned, at least importance_workspace_bytes from
+ * segkv_plan_sizes (else SEGKV_ERR_WORKSPACE); it receives one partial score
+ * per (kv head, key of a block the head's table touches), summed over heads in
+ * head order into `importance`. Limits: Hkv <= 256, R <= 65535,
+ * Hq * (n_last rounded up to 32) <= 4096 (else SEGKV_ERR_UNSUPPORTED).
  */
 int32_t token_importance_topk(const segkv_dims* dims, const segkv_meta* meta_host, const segkv_meta* meta_dev,
                               const int32_t* cu_q_dev, const void* q, const void* k_pool, int64_t pool_pages,
                               const int32_t* page_indptr_dev, const int32_t* page_ids_dev,
-                              const int32_t* page_pos_dev, const float* lse_dev, float softmax_scale,
+                              const int32_t* page_pos_dev, const void* plan_dev, size_t plan_bytes,
+                              const float* lse_dev, float softmax_scale,
                               int32_t n_last, const int32_t* k_host, float* importance_dev,
-                              int32_t* topk_idx_dev, void* stream);
+                              int32_t* topk_idx_dev, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Top-k of one fp32 score vector (scores: device [n], n <= 2^30): the k

@@ -129,3 +129,24 @@ def test_attention_validation():
     rc = lib.segkv_build_pages(ctypes.byref(d), ctypes.byref(ms), ctypes.byref(dm), 16, 16, 16, 16, 16, 16,
                                s["table_entries"], None, None, None, 16, None, None, 0, 16, s["plan_bytes"], None)
     assert rc == -1  # moves requested without cache pointers
+
+
+def test_importance_validation():
+    """token_importance_topk validates its workspace and limits on the host, before any launch."""
+    lib = hk.load()
+    d, m = _layout()
+    ms = m.struct()
+    s = hk.segkv_plan_sizes(d, m)
+    dm = hk.Meta(16, 16, 16, 16, 16, 16)
+    k = (ctypes.c_int32 * 1)(10)
+    args = lambda **kw: [ctypes.byref(d), ctypes.byref(ms), ctypes.byref(dm), 16, 16, 16, 10, 16, 16, 16, 16,
+                         kw.get("plan_bytes", s["plan_bytes"]), 16, 0.125, kw.get("n_last", 16), k, 16,
+                         kw.get("idx", None), kw.get("ws", 16), kw.get("ws_bytes", s["importance_workspace_bytes"]),
+                         None]
+    assert s["importance_workspace_bytes"] == d.num_kv_heads * s["total_keys"] * 4
+    assert lib.token_importance_topk(*args(ws=None)) == -5
+    assert lib.token_importance_topk(*args(ws_bytes=s["importance_workspace_bytes"] - 4)) == -5
+    assert lib.token_importance_topk(*args(ws=8)) == -4
+    assert lib.token_importance_topk(*args(n_last=0)) == -1
+    assert lib.token_importance_topk(*args(n_last=4096)) == -2
+    assert lib.token_importance_topk(*args(plan_bytes=8)) == -5
