@@ -13,30 +13,67 @@ namespace {
 
 constexpr int kScanThreads = 1024;
 
-// Exclusive prefix sum over n values produced by value(i), processed in
-// chunks of the block size; write(i, prefix) receives each result and the
-// total is returned (uniform across the block). Block-wide; all threads call it.
-template <class F, class W>
-__device__ int block_exclusive_scan(int n, F value, W write, int* s) {
-  int carry = 0;
-  const int tid = threadIdx.x;
+// DPP moves inside rows of 16 lanes; a lane whose source lies outside its row reads 0
+template <int CTRL>
+__device__ __forceinline__ int dpp_row(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+
+// Inclusive prefix sum over the 64 lanes of a wave: row_shr steps inside each
+// 16-lane row, then the totals of the rows below (read from lanes 15, 31, 47).
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += dpp_row<kDppRowShr1>(x);
+  x += dpp_row<kDppRowShr2>(x);
+  x += dpp_row<kDppRowShr4>(x);
+  x += dpp_row<kDppRowShr8>(x);
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// N exclusive prefix sums at once over n items: value(i, v) fills v[0..N),
+// write(i, p) receives the prefixes; totals[] receives the sums (uniform
+// across the block). Block-wide, all threads call it; s holds at least
+// N * kScanThreads / 64 ints. Two barriers per 1024 items.
+template <int N, class F, class W>
+__device__ void block_scan(int n, F value, W write, int (&totals)[N], int* s) {
+  constexpr int NW = kScanThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int carry[N];
+#pragma unroll
+  for (int c = 0; c < N; ++c) carry[c] = 0;
   for (int base = 0; base < n; base += kScanThreads) {
     const int i = base + tid;
-    const int v = i < n ? value(i) : 0;
-    s[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kScanThreads; off <<= 1) {
-      const int t = tid >= off ? s[tid - off] : 0;
-      __syncthreads();
-      s[tid] += t;
-      __syncthreads();
+    int v[N], x[N];
+#pragma unroll
+    for (int c = 0; c < N; ++c) v[c] = 0;
+    if (i < n) value(i, v);
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+      x[c] = wave_inclusive_scan(v[c]);
+      if (lane == 63) s[c * NW + wave] = x[c];
     }
-    if (i < n) write(i, carry + s[tid] - v);
-    const int tot = s[kScanThreads - 1];
     __syncthreads();
-    carry += tot;
+    int p[N];
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+      int before = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int sw = s[c * NW + w];
+        before += w < wave ? sw : 0;
+        tot += sw;
+      }
+      p[c] = carry[c] + before + x[c] - v[c];
+      carry[c] += tot;
+    }
+    if (i < n) write(i, p);
+    __syncthreads();
   }
-  return carry;
+#pragma unroll
+  for (int c = 0; c < N; ++c) totals[c] = carry[c];
 }
 
 struct PagesArgs {
@@ -56,6 +93,7 @@ struct PagesArgs {
   char* plan;
   int R, Hkv, G;
   int chunk_tiles;
+  int n_mtiles, n_split;  // host counts (bounds of the plan arrays)
   int n_items;      // launch slots of the attention kernel (a multiple of 8)
   int n_imp_items;  // importance work items (64-key blocks of every table)
   PlanLayout L;
@@ -89,11 +127,12 @@ __device__ PairInfo pair_info(const PagesArgs& a, int k) {
 // itself, so it does not wait for the planning block.
 __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fill_blocks_per_pair) {
   __shared__ int s[kScanThreads];
+  __shared__ int sseg[kScanThreads];  // fill blocks: segment starts of the pair's request
   __shared__ int pair_maxc[kMaxPairs];  // most chunks of any m-tile of the pair
   __shared__ int pair_ib[kMaxPairs];    // first group-major item position of the pair
+  __shared__ int pair_imp[kMaxPairs];   // first importance item of the pair
   __shared__ PairInfo info[kMaxPairs];
   __shared__ int req_off[kMaxPairs + 1];
-  __shared__ int mt_tiles[kMaxMTiles];
   __shared__ int mt_chunks[kMaxMTiles];
   __shared__ int red[2][kScanThreads / 64];
   const int tid = threadIdx.x;
@@ -118,6 +157,10 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
       red[1][tid >> 6] = msum;
     }
     const PairInfo p = pair_info(a, k);
+    {
+      const int rr = k / a.Hkv, t0 = a.m.seg_indptr[rr], t1 = a.m.seg_indptr[rr + 1];
+      if (t1 - t0 <= kScanThreads && tid < t1 - t0) sseg[tid] = a.m.seg_start[t0 + tid];
+    }
     __syncthreads();
     int base = 0, mbase = 0;
     for (int w = 0; w < kScanThreads / 64; ++w) {
@@ -130,12 +173,20 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
     const int s0 = a.m.seg_indptr[r], s1 = a.m.seg_indptr[r + 1];
     const int tok = runs_page(p.pr, e) * kPage;
     int lo = s0, hi = s1 - 1;  // segment holding this page: last segment with start <= tok
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.m.seg_start[mid] <= tok) lo = mid; else hi = mid - 1;
+    if (s1 - s0 <= kScanThreads) {  // starts staged in LDS (the request's segments, one load each)
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sseg[mid - s0] <= tok) lo = mid; else hi = mid - 1;
+      }
+    } else {
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.m.seg_start[mid] <= tok) lo = mid; else hi = mid - 1;
+      }
     }
     const int sg = lo;
-    const int qpage = (tok - a.m.seg_start[sg]) / kPage;
+    const int sstart = s1 - s0 <= kScanThreads ? sseg[sg - s0] : a.m.seg_start[sg];
+    const int qpage = (tok - sstart) / kPage;
     const int phys = a.seg_pages[a.seg_page_indptr[sg * a.Hkv + h] + qpage];
     a.page_ids[base + e] = phys;
     a.page_pos[base + e] = tok;
@@ -144,7 +195,7 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
       const int mi = mbase + e;
       a.move_src[mi] = a.cache_pages[a.cache_page_indptr[sg * a.Hkv + h] + qpage];
       a.move_dst[mi] = phys;
-      a.move_delta[mi] = a.m.seg_start[sg] - a.seg_orig_start[sg];
+      a.move_delta[mi] = sstart - a.seg_orig_start[sg];
     }
     return;
   }
@@ -161,26 +212,35 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
 
   for (int k = tid; k < n_pairs; k += kScanThreads) info[k] = pair_info(a, k);
   __syncthreads();
-  const int tot = block_exclusive_scan(
-      n_pairs, [&](int k) { return runs_count(info[k].pr); },
-      [&](int k, int p) {
-        a.page_indptr[k] = p;
-        info[k].tbase = p;
+  // per pair: table entries, head-aware moves, importance blocks
+  int pt[3];
+  block_scan<3>(
+      n_pairs,
+      [&](int k, int (&v)[3]) {
+        v[0] = runs_count(info[k].pr);
+        v[1] = runs_rank(info[k].pr, info[k].bq / kPage);
+        v[2] = runs_count(block_runs(info[k].pr));
       },
-      s);
-  const int mtot = block_exclusive_scan(
-      n_pairs, [&](int k) { return runs_rank(info[k].pr, info[k].bq / kPage); },
-      [&](int k, int p) { move_off[k] = p; }, s);
-  const int n_mt = block_exclusive_scan(
-      a.R, [&](int r) { return a.Hkv * cdiv(info[r * a.Hkv].Lq, MP); },
-      [&](int r, int p) {
-        req_off[r] = p;
-        req_off_g[r] = p;
+      [&](int k, const int (&p)[3]) {
+        a.page_indptr[k] = p[0];
+        info[k].tbase = p[0];
+        move_off[k] = p[1];
+        pair_imp[k] = p[2];
       },
-      s);
+      pt, s);
+  // per request: m-tiles
+  int rt[1];
+  block_scan<1>(
+      a.R, [&](int r, int (&v)[1]) { v[0] = a.Hkv * cdiv(info[r * a.Hkv].Lq, MP); },
+      [&](int r, const int (&p)[1]) {
+        req_off[r] = p[0];
+        req_off_g[r] = p[0];
+      },
+      rt, s);
+  const int n_mt = imin(rt[0], a.n_mtiles);  // equal unless the layout changed since sizing
   if (tid == 0) {
-    a.page_indptr[n_pairs] = tot;
-    move_off[n_pairs] = mtot;
+    a.page_indptr[n_pairs] = pt[0];
+    move_off[n_pairs] = pt[1];
     req_off[a.R] = n_mt;
     req_off_g[a.R] = n_mt;
   }
@@ -222,24 +282,27 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
     d.n_chunks = num_chunks(d.n_tiles, S);
     d.partial_base = -1;
     d.pad[0] = d.pad[1] = d.pad[2] = 0;
-    mt[i] = d;
-    mt_tiles[i] = d.n_tiles;
     mt_chunks[i] = d.n_chunks;
+    mt[i] = d;
   }
   __syncthreads();
 
-  const int n_partials = block_exclusive_scan(
-      n_mt, [&](int i) { return mt_chunks[i] > 1 ? mt_chunks[i] : 0; },
-      [&](int i, int p) {
-        if (mt_chunks[i] > 1) mt[i].partial_base = p;
+  // per m-tile: partial slots and split list
+  int mt_tot[2];
+  block_scan<2>(
+      n_mt,
+      [&](int i, int (&v)[2]) {
+        v[0] = mt_chunks[i] > 1 ? mt_chunks[i] : 0;
+        v[1] = mt_chunks[i] > 1 ? 1 : 0;
       },
-      s);
-  const int n_split = block_exclusive_scan(
-      n_mt, [&](int i) { return mt_chunks[i] > 1 ? 1 : 0; },
-      [&](int i, int p) {
-        if (mt_chunks[i] > 1) split[p] = i;
+      [&](int i, const int (&p)[2]) {
+        if (mt_chunks[i] > 1) {
+          mt[i].partial_base = p[0];
+          if (p[1] < a.n_split) split[p[1]] = i;
+        }
       },
-      s);
+      mt_tot, s);
+  const int n_partials = mt_tot[0], n_split = mt_tot[1];
 
   // items in XCD-aware order (see xcd_slot): group-major position of item
   // (m-tile j of pair k, chunk c) = pair_ib[k] + c * nj_k + j
@@ -251,42 +314,45 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
     pair_maxc[k] = mc;
   }
   __syncthreads();
-  const int n_pos = block_exclusive_scan(
-      n_pairs, [&](int k) {
+  int pos_tot[1];
+  block_scan<1>(
+      n_pairs,
+      [&](int k, int (&v)[1]) {
         const int r = k / a.Hkv;
-        return pair_maxc[k] * ((req_off[r + 1] - req_off[r]) / a.Hkv);
+        v[0] = pair_maxc[k] * ((req_off[r + 1] - req_off[r]) / a.Hkv);
       },
-      [&](int k, int p) { pair_ib[k] = p; }, s);
+      [&](int k, const int (&p)[1]) { pair_ib[k] = p[0]; }, pos_tot, s);
+  const int n_pos = pos_tot[0];
+  // one launch slot per thread: slot b runs on XCD b % 8 and takes position
+  // (b % 8) q8 + b / 8 of the group-major list
   const int q8 = a.n_items / kXcds;
-  for (int i = tid; i < n_mt; i += kScanThreads) {
-    int lo = 0, hi = a.R - 1;  // request: last r with req_off[r] <= i
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (req_off[mid] <= i) lo = mid; else hi = mid - 1;
+  for (int b = tid; b < a.n_items; b += kScanThreads) {
+    const int p = (b & (kXcds - 1)) * q8 + (b >> 3);
+    Item it{-1, 0};
+    if (p < n_pos) {
+      int lo = 0, hi = n_pairs - 1;  // pair: last k with pair_ib[k] <= p
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pair_ib[mid] <= p) lo = mid; else hi = mid - 1;
+      }
+      const int k = lo, r = k / a.Hkv, h = k % a.Hkv;
+      const int nj = (req_off[r + 1] - req_off[r]) / a.Hkv;
+      const int rel = p - pair_ib[k], c = rel / nj, i = req_off[r] + h * nj + rel % nj;
+      if (c < mt_chunks[i]) it = Item{i, c};
     }
-    const int r = lo;
-    const int nj = (req_off[r + 1] - req_off[r]) / a.Hkv;
-    const int h = (i - req_off[r]) / nj, j = (i - req_off[r]) % nj, k = r * a.Hkv + h;
-    for (int c = 0; c < pair_maxc[k]; ++c) {
-      const int p = pair_ib[k] + c * nj + j;
-      if (p < a.n_items) items[xcd_slot(p, q8)] = c < mt_chunks[i] ? Item{i, c} : Item{-1, 0};
-    }
+    items[b] = it;
   }
-  for (int p = n_pos + tid; p < a.n_items; p += kScanThreads) items[xcd_slot(p, q8)] = Item{-1, 0};
 
   // importance items: every 64-key block of every table, pair by pair
-  __syncthreads();  // pair_maxc is reused below
-  const int n_imp = block_exclusive_scan(
-      n_pairs, [&](int k) { return runs_count(block_runs(info[k].pr)); }, [&](int k, int p) { pair_maxc[k] = p; },
-      s);
+  const int n_imp = pt[2];
   ImpItem* imp_items = reinterpret_cast<ImpItem*>(a.plan + a.L.imp_items_off);
   for (int x = tid; x < imin(n_imp, a.n_imp_items); x += kScanThreads) {
-    int lo = 0, hi = n_pairs - 1;  // pair: last k with base <= x
+    int lo = 0, hi = n_pairs - 1;  // pair: last k with pair_imp[k] <= x
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (pair_maxc[mid] <= x) lo = mid; else hi = mid - 1;
+      if (pair_imp[mid] <= x) lo = mid; else hi = mid - 1;
     }
-    imp_items[x] = ImpItem{lo, runs_page(block_runs(info[lo].pr), x - pair_maxc[lo])};
+    imp_items[x] = ImpItem{lo, runs_page(block_runs(info[lo].pr), x - pair_imp[lo])};
   }
   if (tid == 0) {
     PlanHeader h;
@@ -413,6 +479,8 @@ extern "C" int32_t segkv_build_pages(const segkv_dims* dims, const segkv_meta* m
   a.chunk_tiles = hp.chunk_tiles;
   a.n_items = hp.n_items;
   a.n_imp_items = hp.n_imp_items;
+  a.n_mtiles = hp.n_mtiles;
+  a.n_split = hp.n_split;
   a.L = plan_layout(a.R * a.Hkv, a.R, hp.n_mtiles, hp.n_items, hp.n_split, hp.n_imp_items);
   hipStream_t s = static_cast<hipStream_t>(stream);
   int max_pages = 1;
