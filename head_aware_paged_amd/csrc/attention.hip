@@ -50,7 +50,7 @@ struct AttnArgs {
   PlanLayout L;
   uint16_t* out;
   float* lse;
-  float* partials;
+  char* partials;      // split-KV workspace, partial_slot_bytes(D) per chunk
   float scale_log2;  // softmax_scale * log2(e)
   int Hq, G;
 };
@@ -366,32 +366,32 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
       }
     if (a.lse != nullptr && lg == 0) a.lse[(size_t)qrow * a.Hq + qhead] = (m_run + log2f(l_row)) * kLn2;
   } else {
-    float* slot = a.partials + (size_t)(mt.partial_base + it.chunk) * partial_slot_bytes(D) / sizeof(float) +
-                  (size_t)rm * (D + 2);
+    char* slot = a.partials + (size_t)(mt.partial_base + it.chunk) * partial_slot_bytes(D);
+    uint16_t* po = reinterpret_cast<uint16_t*>(slot) + (size_t)rm * D;
+    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;  // a row may see no key of this chunk: O_c = 0, l_c = 0
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = 32 * b + 8 * g4 + 4 * lg;
-        f32x4 v;
-        v[0] = o_acc[b][4 * g4 + 0];
-        v[1] = o_acc[b][4 * g4 + 1];
-        v[2] = o_acc[b][4 * g4 + 2];
-        v[3] = o_acc[b][4 * g4 + 3];
-        *reinterpret_cast<f32x4*>(slot + d) = v;
+        *reinterpret_cast<bf16x4*>(po + d) =
+            bf16x4{(__bf16)(o_acc[b][4 * g4 + 0] * inv), (__bf16)(o_acc[b][4 * g4 + 1] * inv),
+                   (__bf16)(o_acc[b][4 * g4 + 2] * inv), (__bf16)(o_acc[b][4 * g4 + 3] * inv)};
       }
     if (lg == 0) {
-      slot[D] = m_run;
-      slot[D + 1] = l_row;
+      float* ml = reinterpret_cast<float*>(slot + partial_o_bytes(D)) + 2 * rm;
+      *reinterpret_cast<f32x2*>(ml) = f32x2{m_run, l_row};
     }
   }
 }
 
 // Grid (split m-tile, row group): each thread merges one row's 4-wide d group
-// over the m-tile's chunks, in chunk order.
+// over the m-tile's chunks, in chunk order:
+//   O = sum_c 2^(m_c - m*) l_c (O_c / l_c) / sum_c 2^(m_c - m*) l_c,
+//   LSE = (m* + log2 sum_c 2^(m_c - m*) l_c) ln 2.
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) {
-  constexpr int DG = D / 4;                       // float4 groups per row
+  constexpr int DG = D / 4;                       // 4-element groups per row
   constexpr int kRowsPerBlock = kAttnThreads / DG;
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(a.plan);
   if ((int)blockIdx.x >= hdr->n_split) return;
@@ -402,23 +402,26 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) 
   const int rm = blockIdx.y * kRowsPerBlock + threadIdx.x / DG, dg = threadIdx.x % DG;
   const int hg = rm / MP, p = rm % MP;
   if (p >= mt.n_pos) return;
-  const size_t slot_floats = partial_slot_bytes(D) / sizeof(float);
-  const float* base = a.partials + (size_t)mt.partial_base * slot_floats + (size_t)rm * (D + 2);
+  const size_t slot = partial_slot_bytes(D);
+  const char* base = a.partials + (size_t)mt.partial_base * slot;
+  const char* ml0 = base + partial_o_bytes(D) + (size_t)rm * 2 * sizeof(float);
+  const char* o0 = base + ((size_t)rm * D + 4 * dg) * 2;
   const int nc = mt.n_chunks;
   float mstar = -INFINITY;
-  for (int c = 0; c < nc; ++c) mstar = fmaxf(mstar, base[c * slot_floats + D]);
+#pragma unroll 8
+  for (int c = 0; c < nc; ++c) mstar = fmaxf(mstar, reinterpret_cast<const float*>(ml0 + c * slot)[0]);
   float lsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+#pragma unroll 8
   for (int c = 0; c < nc; ++c) {
-    const float* row = base + c * slot_floats;
-    const float wgt = exp2f(row[D] - mstar);
-    lsum += wgt * row[D + 1];
-    const f32x4 o = *reinterpret_cast<const f32x4*>(row + 4 * dg);
-    acc[0] += wgt * o[0];
-    acc[1] += wgt * o[1];
-    acc[2] += wgt * o[2];
-    acc[3] += wgt * o[3];
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(ml0 + c * slot);
+    const bf16x4 o = *reinterpret_cast<const bf16x4*>(o0 + c * slot);
+    const float wl = exp2f(ml[0] - mstar) * ml[1];
+    lsum += wl;
+    acc[0] += wl * (float)o[0];
+    acc[1] += wl * (float)o[1];
+    acc[2] += wl * (float)o[2];
+    acc[3] += wl * (float)o[3];
   }
   const float inv = 1.f / lsum;
   const int qhead = mt.h * a.G + hg, qrow = mt.q_row0 + p;
@@ -469,7 +472,7 @@ extern "C" int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_met
                     hp.n_split, hp.n_imp_items);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  a.partials = static_cast<float*>(workspace);
+  a.partials = static_cast<char*>(workspace);
   a.scale_log2 = softmax_scale * kLog2e;
   a.Hq = dims->num_q_heads;
   a.G = dims->num_q_heads / dims->num_kv_heads;

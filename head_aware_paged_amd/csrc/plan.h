@@ -246,7 +246,10 @@ SEGKV_HD PlanLayout plan_layout(int n_pairs, int n_requests, int n_mtiles, int n
   return L;
 }
 
-// Bytes of one partial result slot: kMRows rows x (D fp32 O + m + l).
-SEGKV_HD size_t partial_slot_bytes(int D) { return (size_t)kMRows * (size_t)(D + 2) * sizeof(float); }
+// One partial result slot (one chunk of one split m-tile): kMRows rows of the
+// chunk's normalised output O_c / l_c in bf16, then kMRows (m_c, l_c) fp32
+// pairs (m in log2 units).
+SEGKV_HD size_t partial_o_bytes(int D) { return (size_t)kMRows * (size_t)D * 2; }
+SEGKV_HD size_t partial_slot_bytes(int D) { return partial_o_bytes(D) + (size_t)kMRows * 2 * sizeof(float); }
 
 }  // namespace segkv
