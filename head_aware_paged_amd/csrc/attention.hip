@@ -407,21 +407,40 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) 
   const char* ml0 = base + partial_o_bytes(D) + (size_t)rm * 2 * sizeof(float);
   const char* o0 = base + ((size_t)rm * D + 4 * dg) * 2;
   const int nc = mt.n_chunks;
-  float mstar = -INFINITY;
-#pragma unroll 8
-  for (int c = 0; c < nc; ++c) mstar = fmaxf(mstar, reinterpret_cast<const float*>(ml0 + c * slot)[0]);
-  float lsum = 0.f;
+  // chunks in batches of 16 whose loads are all in flight together; the
+  // running max and sums are rescaled between batches
+  constexpr int CB = 16;
+  float mstar = -INFINITY, lsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int c = 0; c < nc; ++c) {
-    const f32x2 ml = *reinterpret_cast<const f32x2*>(ml0 + c * slot);
-    const bf16x4 o = *reinterpret_cast<const bf16x4*>(o0 + c * slot);
-    const float wl = exp2f(ml[0] - mstar) * ml[1];
-    lsum += wl;
-    acc[0] += wl * (float)o[0];
-    acc[1] += wl * (float)o[1];
-    acc[2] += wl * (float)o[2];
-    acc[3] += wl * (float)o[3];
+  for (int c0 = 0; c0 < nc; c0 += CB) {
+    f32x2 ml[CB];
+    bf16x4 o[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int c = imin(c0 + u, nc - 1);
+      ml[u] = *reinterpret_cast<const f32x2*>(ml0 + c * slot);
+      o[u] = *reinterpret_cast<const bf16x4*>(o0 + c * slot);
+    }
+    float mb = mstar;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) mb = c0 + u < nc ? fmaxf(mb, ml[u][0]) : mb;
+    const float sc = mb == -INFINITY ? 1.f : exp2f(mstar - mb);  // nothing seen yet: nothing to rescale
+    lsum *= sc;
+    acc[0] *= sc;
+    acc[1] *= sc;
+    acc[2] *= sc;
+    acc[3] *= sc;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      // a chunk where the row sees no key has l = 0, m = -inf: weight 0
+      const float wl = c0 + u < nc && ml[u][1] > 0.f ? exp2f(ml[u][0] - mb) * ml[u][1] : 0.f;
+      lsum += wl;
+      acc[0] += wl * (float)o[u][0];
+      acc[1] += wl * (float)o[u][1];
+      acc[2] += wl * (float)o[u][2];
+      acc[3] += wl * (float)o[u][3];
+    }
+    mstar = mb;
   }
   const float inv = 1.f / lsum;
   const int qhead = mt.h * a.G + hg, qrow = mt.q_row0 + p;
