@@ -181,19 +181,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
   // DMA of tile t into a stage: wave w moves rows [16 w, 16 w + 16) = page w
   // of the tile, so the page id is wave-uniform. A missing page reads page 0:
   // its keys are masked by position and its V rows are zeroed before use.
+  // (per-lane element offsets inside the page are fixed: computed once)
+  int koff[KLOADS], voff[KLOADS];
+#pragma unroll
+  for (int u = 0; u < KLOADS; ++u) {
+    const int row = (wave * KLOADS + u) * RPK + lane / KCH;
+    const int ph = lane % KCH;
+    koff[u] = (row & 15) * D + 8 * (ph ^ k_swz<D>(row));
+    voff[u] = (row & 15) * D + 8 * (ph ^ v_swz<D>(row));
+  }
   auto dma = [&](uint16_t* kdst, uint16_t* vdst, int t) {
     const int x = kTilePages * (t - t_lo) + wave;
     const int pid = __builtin_amdgcn_readfirstlane(spid[x]);
-    const size_t page = (size_t)(pid < 0 ? 0 : pid) * kPage * D;
+    const size_t page = (size_t)(pid < 0 ? 0 : pid) * kPage * D;  // wave-uniform
+    const uint16_t* kpage = a.k_pool + page;
+    const uint16_t* vpage = a.v_pool + page;
 #pragma unroll
     for (int u = 0; u < KLOADS; ++u) {
       const int blk = wave * KLOADS + u;
-      const int row = blk * RPK + lane / KCH;
-      const int ph = lane % KCH;
-      const size_t roff = page + (size_t)(row & 15) * D;
-      const int kc = ph ^ k_swz<D>(row), vc = ph ^ v_swz<D>(row);
-      const uint16_t* ksrc = a.k_pool + roff + 8 * kc;
-      const uint16_t* vsrc = a.v_pool + roff + 8 * vc;
+      const uint16_t* ksrc = kpage + koff[u];
+      const uint16_t* vsrc = vpage + voff[u];
       __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void*)&kdst[blk * 512], 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)&vdst[blk * 512], 16, 0, 0);
     }
@@ -285,11 +292,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
     }
 
     // ---- online softmax (lazy rescale: only when the max grows by > 2^8) ----
-    float tmax = -INFINITY;
+    // row max as a 4-way tree of 3-input maxima (short dependency chains)
+    float tm[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[kb][i]);
+    for (int c = 0; c < 4; ++c) {
+      const f32x16& v = sc[c >> 1];
+      const int o = 8 * (c & 1);
+      tm[c] = fmaxf(fmaxf(fmaxf(v[o], v[o + 1]), fmaxf(v[o + 2], v[o + 3])),
+                    fmaxf(fmaxf(v[o + 4], v[o + 5]), fmaxf(v[o + 6], v[o + 7])));
+    }
+    float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_tile = tmax * a.scale_log2;
     const bool rescale = m_tile > m_run + kRescaleThreshold;
@@ -304,6 +316,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     bf16x8 pf[4];
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};  // four partial row sums (short dependency chains)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -312,8 +325,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
         for (int j = 0; j < 8; ++j) {
           const float pv = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hh + j], a.scale_log2, -m_use));
           pf[2 * kb + hh][j] = (__bf16)pv;
-          l_run += pv;
+          ls[j & 3] += pv;
         }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
     // ---- O^T += V^T P^T (V^T fragments from transpose reads) ----
 #pragma unroll
