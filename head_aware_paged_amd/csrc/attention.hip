@@ -501,8 +501,7 @@ extern "C" int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_met
   a.page_ids = page_ids_dev;
   a.page_pos = page_pos_dev;
   a.plan = static_cast<const char*>(plan_dev);
-  a.L = plan_layout(dims->num_requests * dims->num_kv_heads, dims->num_requests, hp.n_mtiles, hp.n_items,
-                    hp.n_split, hp.n_imp_items);
+  a.L = host_plan_layout(*dims, hp);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.partials = static_cast<char*>(workspace);

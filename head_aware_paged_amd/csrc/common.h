@@ -36,10 +36,16 @@ HeadView head_view_host(const segkv_dims& d, const segkv_meta& m, int r, int h);
 // Host mirror of the device attention plan (exact counts).
 struct HostPlan {
   int n_mtiles = 0, n_items = 0, n_split = 0, n_partials = 0, chunk_tiles = 1, max_tiles = 0, n_imp_items = 0;
+  int key_blocks = 0;  // 64-key blocks of the longest request
   int64_t table_entries = 0, move_entries = 0, total_q_rows = 0, total_keys = 0;
   size_t plan_bytes = 0, workspace_bytes = 0;
 };
 int32_t compute_host_plan(const segkv_dims* dims, const segkv_meta* m, HostPlan* out);
+
+inline PlanLayout host_plan_layout(const segkv_dims& d, const HostPlan& p) {
+  return plan_layout(d.num_requests * d.num_kv_heads, d.num_requests, p.n_mtiles, p.n_items, p.n_split,
+                     p.n_imp_items, p.key_blocks);
+}
 
 // Workspace of token_importance_topk: one fp32 partial per (kv head, key).
 inline size_t importance_workspace_bytes(const segkv_dims& d, int64_t total_keys) {

@@ -182,6 +182,7 @@ int32_t compute_host_plan(const segkv_dims* d, const segkv_meta* m, HostPlan* ou
       if (h == 0) {
         p.total_q_rows += v.Lq;
         p.total_keys += v.Lk;
+        p.key_blocks = std::max(p.key_blocks, cdiv(v.Lk, kTileKeys));
       }
       for (int t0 = 0; t0 < v.Lq; t0 += MP) {
         const int i_lo = v.bq + t0, i_hi = v.bq + imin(v.Lq, t0 + MP) - 1;
@@ -217,7 +218,7 @@ int32_t compute_host_plan(const segkv_dims* d, const segkv_meta* m, HostPlan* ou
   }
   REQUIRE(positions < (int64_t)1 << 30, SEGKV_ERR_UNSUPPORTED, "too many attention work items");
   p.n_items = kXcds * (int)((positions + kXcds - 1) / kXcds);
-  const PlanLayout L = plan_layout(R * Hkv, R, p.n_mtiles, p.n_items, p.n_split, p.n_imp_items);
+  const PlanLayout L = host_plan_layout(*d, p);
   p.plan_bytes = L.total;
   p.workspace_bytes = (size_t)p.n_partials * partial_slot_bytes(d->head_dim);
   *out = p;

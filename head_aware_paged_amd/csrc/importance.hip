@@ -203,11 +203,7 @@ __global__ __launch_bounds__(kImpThreads, 3) void importance_kernel(ImpArgs a) {
   }
   __syncthreads();
   if (tid < kTileKeys && kb0 + tid < Lk) {
-    int off = 0;  // output offset of request r: sum of earlier context lengths
-    for (int rr = 0; rr < r; ++rr) {
-      const int s2 = a.m.seg_indptr[rr + 1] - 1;
-      off += a.m.seg_start[s2] + a.m.seg_len[s2];
-    }
+    const int off = reinterpret_cast<const int32_t*>(a.plan + a.L.req_key_off)[r];  // request r's first key
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < kImpWaves; ++w) sum += colsum[w][tid];
@@ -215,33 +211,26 @@ __global__ __launch_bounds__(kImpThreads, 3) void importance_kernel(ImpArgs a) {
   }
 }
 
-constexpr int kImpMaxHeads = 256;  // kv heads whose block runs the reduction stages in LDS
+constexpr int kImpMaxHeads = 64;  // kv heads of one request (one 64-bit mask per key block)
 
-// importance[off + j] = sum, in head order, of the partials of the heads whose
-// tables touch key j's 64-key block (0 when none does). One work-group per
-// 256 keys of one request.
-__global__ __launch_bounds__(256) void importance_reduce_kernel(segkv_meta m, const float* __restrict__ partial,
+// importance[off_r + j] = sum, in head order, of the partials of the heads whose
+// tables touch key j's 64-key block (0 when none does); the plan holds one
+// head mask per (request, block) and the requests' key offsets.
+__global__ __launch_bounds__(256) void importance_reduce_kernel(const char* __restrict__ plan, PlanLayout L,
+                                                                const float* __restrict__ partial,
                                                                 float* __restrict__ importance, int64_t total_keys,
-                                                                int Hkv) {
-  __shared__ PageRuns br[kImpMaxHeads];
+                                                                int key_blocks) {
   const int r = blockIdx.y;
-  const int sq = m.seg_indptr[r + 1] - 1;
-  const int Lk = m.seg_start[sq] + m.seg_len[sq];
+  const int32_t* req_key = reinterpret_cast<const int32_t*>(plan + L.req_key_off);
+  const int off = req_key[r], Lk = req_key[r + 1] - off;
   const int j = blockIdx.x * 256 + threadIdx.x;
-  if ((int)blockIdx.x * 256 >= Lk) return;
-  int off = 0;
-  for (int rr = 0; rr < r; ++rr) {
-    const int s2 = m.seg_indptr[rr + 1] - 1;
-    off += m.seg_start[s2] + m.seg_len[s2];
-  }
-  for (int h = threadIdx.x; h < Hkv; h += 256) br[h] = block_runs(head_page_runs(head_view_dev(m, Hkv, r, h)));
-  __syncthreads();
   if (j >= Lk) return;
-  const int blk = j / kTileKeys;
+  uint64_t mk = reinterpret_cast<const uint64_t*>(plan + L.imp_mask_off)[(size_t)r * key_blocks + j / kTileKeys];
   float sum = 0.f;
-  for (int h = 0; h < Hkv; ++h) {
-    const PageRuns b = br[h];
-    if (runs_rank(b, blk + 1) - runs_rank(b, blk) == 1) sum += partial[(size_t)h * total_keys + off + j];
+  while (mk != 0) {
+    const int h = __builtin_ctzll(mk);
+    mk &= mk - 1;
+    sum += partial[(size_t)h * total_keys + off + j];
   }
   importance[off + j] = sum;
 }
@@ -529,7 +518,7 @@ extern "C" int32_t token_importance_topk(const segkv_dims* dims, const segkv_met
       !page_pos_dev || !plan_dev || !lse_dev || !importance_dev)
     return fail(SEGKV_ERR_INVALID_ARG, "a required pointer is NULL");
   if (plan_bytes < hp.plan_bytes) return fail(SEGKV_ERR_WORKSPACE, "plan smaller than plan_bytes from segkv_plan_sizes");
-  if (dims->num_kv_heads > kImpMaxHeads) return fail(SEGKV_ERR_UNSUPPORTED, "importance supports num_kv_heads <= 256");
+  if (dims->num_kv_heads > kImpMaxHeads) return fail(SEGKV_ERR_UNSUPPORTED, "importance supports num_kv_heads <= 64");
   if (n_last <= 0) return fail(SEGKV_ERR_INVALID_ARG, "n_last must be > 0");
   const int G = dims->num_q_heads / dims->num_kv_heads;
   if (workspace == nullptr || workspace_bytes < importance_workspace_bytes(*dims, hp.total_keys))
@@ -567,7 +556,7 @@ extern "C" int32_t token_importance_topk(const segkv_dims* dims, const segkv_met
   a.importance = importance_dev;
   a.partial = static_cast<float*>(workspace);
   a.plan = static_cast<const char*>(plan_dev);
-  a.L = plan_layout(R * dims->num_kv_heads, R, hp.n_mtiles, hp.n_items, hp.n_split, hp.n_imp_items);
+  a.L = host_plan_layout(*dims, hp);
   a.total_keys = hp.total_keys;
   a.scale_log2 = softmax_scale * kLog2e;
   a.R = R;
@@ -583,8 +572,8 @@ extern "C" int32_t token_importance_topk(const segkv_dims* dims, const segkv_met
       importance_kernel<64><<<hp.n_imp_items, kImpThreads, 0, s>>>(a);
     SEGKV_LAUNCH_CHECK();
   }
-  importance_reduce_kernel<<<dim3(cdiv(max_lk, 256), R), 256, 0, s>>>(*meta_dev, a.partial, importance_dev,
-                                                                      hp.total_keys, a.Hkv);
+  importance_reduce_kernel<<<dim3(cdiv(max_lk, 256), R), 256, 0, s>>>(a.plan, a.L, a.partial, importance_dev,
+                                                                      hp.total_keys, hp.key_blocks);
   SEGKV_LAUNCH_CHECK();
   if (topk_idx_dev == nullptr) return SEGKV_OK;
   // one selection per request on the same stream (host knows every offset)

@@ -94,6 +94,7 @@ struct PagesArgs {
   int R, Hkv, G;
   int chunk_tiles;
   int n_mtiles, n_split;  // host counts (bounds of the plan arrays)
+  int key_blocks;         // 64-key blocks of the longest request
   int n_items;      // launch slots of the attention kernel (a multiple of 8)
   int n_imp_items;  // importance work items (64-key blocks of every table)
   PlanLayout L;
@@ -138,6 +139,24 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
   const int tid = threadIdx.x;
   const int n_pairs = a.R * a.Hkv;
 
+  const int n_fill = n_pairs * fill_blocks_per_pair;
+  if ((int)blockIdx.x > n_fill) {
+    // ---------------- importance head masks of request r, blocks [c * 1024, ...) ----------------
+    // (kv heads <= 64; otherwise no masks are written)
+    const int mb = blockIdx.x - 1 - n_fill, per_req = cdiv(a.key_blocks, kScanThreads);
+    const int r = mb / per_req, blk = (mb % per_req) * kScanThreads + tid;
+    if (a.Hkv > 64) return;
+    for (int h = tid; h < a.Hkv; h += kScanThreads) info[h].pr = block_runs(pair_info(a, r * a.Hkv + h).pr);
+    __syncthreads();
+    if (blk >= a.key_blocks) return;
+    uint64_t mk = 0;
+    for (int h = 0; h < a.Hkv; ++h) {
+      const PageRuns& b = info[h].pr;
+      if (runs_rank(b, blk + 1) - runs_rank(b, blk) == 1) mk |= 1ull << h;
+    }
+    reinterpret_cast<uint64_t*>(a.plan + a.L.imp_mask_off)[(size_t)r * a.key_blocks + blk] = mk;
+    return;
+  }
   if (blockIdx.x > 0) {
     // ---------------- table fill for pair k, entries [blk * 1024, ...) ----------------
     const int k = (blockIdx.x - 1) / fill_blocks_per_pair;
@@ -343,6 +362,15 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
     items[b] = it;
   }
 
+  // importance: first key of each request, and per (request, 64-key block)
+  // the kv heads whose tables touch the block (kv heads <= 64)
+  int32_t* req_key = reinterpret_cast<int32_t*>(a.plan + a.L.req_key_off);
+  int kt[1];
+  block_scan<1>(
+      a.R, [&](int r, int (&v)[1]) { v[0] = info[r * a.Hkv].bq + info[r * a.Hkv].Lq; },
+      [&](int r, const int (&p)[1]) { req_key[r] = p[0]; }, kt, s);
+  if (tid == 0) req_key[a.R] = kt[0];
+
   // importance items: every 64-key block of every table, pair by pair
   const int n_imp = pt[2];
   ImpItem* imp_items = reinterpret_cast<ImpItem*>(a.plan + a.L.imp_items_off);
@@ -481,7 +509,8 @@ extern "C" int32_t segkv_build_pages(const segkv_dims* dims, const segkv_meta* m
   a.n_imp_items = hp.n_imp_items;
   a.n_mtiles = hp.n_mtiles;
   a.n_split = hp.n_split;
-  a.L = plan_layout(a.R * a.Hkv, a.R, hp.n_mtiles, hp.n_items, hp.n_split, hp.n_imp_items);
+  a.key_blocks = hp.key_blocks;
+  a.L = host_plan_layout(*dims, hp);
   hipStream_t s = static_cast<hipStream_t>(stream);
   int max_pages = 1;
   for (int r = 0; r < a.R; ++r) {
@@ -489,7 +518,8 @@ extern "C" int32_t segkv_build_pages(const segkv_dims* dims, const segkv_meta* m
     max_pages = imax(max_pages, cdiv(meta_host->seg_start[sq] + meta_host->seg_len[sq], kPage));
   }
   const int per_pair = cdiv(max_pages, kScanThreads);
-  build_kernel<<<1 + a.R * a.Hkv * per_pair, kScanThreads, 0, s>>>(a, per_pair);
+  const int mask_blocks = a.R * cdiv(hp.key_blocks, kScanThreads);
+  build_kernel<<<1 + a.R * a.Hkv * per_pair + mask_blocks, kScanThreads, 0, s>>>(a, per_pair);
   SEGKV_LAUNCH_CHECK();
   return SEGKV_OK;
 }

@@ -228,13 +228,17 @@ struct ImpItem {
 struct PlanLayout {
   size_t move_off_off;   // int32 [R*Hkv + 1]: first move of each (r, h)
   size_t req_mt_off;     // int32 [R + 1]: first m-tile of each request
-  size_t mtiles_off, items_off, split_off, imp_items_off, total;
+  size_t mtiles_off, items_off, split_off, imp_items_off;
+  size_t req_key_off;    // int32 [R + 1]: first key of each request in the importance vector
+  size_t imp_mask_off;   // uint64 [R][key_blocks]: kv heads whose tables touch each 64-key block
+  size_t total;
 };
 
 SEGKV_HD size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// key_blocks: 64-key blocks of the longest request.
 SEGKV_HD PlanLayout plan_layout(int n_pairs, int n_requests, int n_mtiles, int n_items, int n_split,
-                                int n_imp_items) {
+                                int n_imp_items, int key_blocks) {
   PlanLayout L;
   L.move_off_off = align256(sizeof(PlanHeader));
   L.req_mt_off = L.move_off_off + align256(sizeof(int32_t) * (size_t)(n_pairs + 1));
@@ -242,7 +246,9 @@ SEGKV_HD PlanLayout plan_layout(int n_pairs, int n_requests, int n_mtiles, int n
   L.items_off = L.mtiles_off + align256(sizeof(MTile) * (size_t)imax(n_mtiles, 1));
   L.split_off = L.items_off + align256(sizeof(Item) * (size_t)imax(n_items, 1));
   L.imp_items_off = L.split_off + align256(sizeof(int32_t) * (size_t)imax(n_split, 1));
-  L.total = L.imp_items_off + align256(sizeof(ImpItem) * (size_t)imax(n_imp_items, 1));
+  L.req_key_off = L.imp_items_off + align256(sizeof(ImpItem) * (size_t)imax(n_imp_items, 1));
+  L.imp_mask_off = L.req_key_off + align256(sizeof(int32_t) * (size_t)(n_requests + 1));
+  L.total = L.imp_mask_off + align256(sizeof(uint64_t) * (size_t)n_requests * (size_t)imax(key_blocks, 1));
   return L;
 }
 

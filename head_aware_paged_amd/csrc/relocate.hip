@@ -34,33 +34,27 @@ __global__ __launch_bounds__(kRelocThreads) void relocate_kernel(
 
   __shared__ double inv_freq[kHalf];
   __shared__ float cs[kMovesPerBatch][kHalf][2];
-  __shared__ int s_src[kMovesPerBatch], s_dst[kMovesPerBatch], s_ok[kMovesPerBatch];
+  __shared__ int s_src[kMovesPerBatch], s_dst[kMovesPerBatch], s_ok[kMovesPerBatch], s_delta[kMovesPerBatch];
 
   const int tid = threadIdx.x;
   const int m0 = blockIdx.x * kMovesPerBatch;
   if (tid < kHalf) inv_freq[tid] = pow(theta, -2.0 * (double)tid / (double)D);
   if (tid < kMovesPerBatch) {
     const int m = m0 + tid;
-    int s = -1, d = -1, ok = 0;
+    int s = -1, d = -1, ok = 0, dl = 0;
     if (m < n_moves) {
       s = src_page[m];
       d = dst_page[m];
+      dl = delta[m];
       ok = (s >= 0 && s < src_pages && d >= 0 && d < dst_pages) ? 1 : 0;
     }
     s_src[tid] = s;
     s_dst[tid] = d;
     s_ok[tid] = ok;
+    s_delta[tid] = dl;
   }
   __syncthreads();
-  for (int e = tid; e < kMovesPerBatch * kHalf; e += kRelocThreads) {
-    const int b = e / kHalf, j = e % kHalf;
-    double sn = 0.0, cn = 1.0;
-    if (s_ok[b]) sincos((double)delta[m0 + b] * inv_freq[j], &sn, &cn);
-    cs[b][j][0] = (float)cn;
-    cs[b][j][1] = (float)sn;
-  }
-
-  // issue every load of the batch before touching LDS again
+  // issue every load of the batch first; the cos/sin table is computed while they fly
   u32x4 kx[kKPerThread], ky[kKPerThread], vv[kVPerThread];
 #pragma unroll
   for (int u = 0; u < kKPerThread; ++u) {
@@ -69,8 +63,8 @@ __global__ __launch_bounds__(kRelocThreads) void relocate_kernel(
     const int t = w / kChunksPerHalf, c = w % kChunksPerHalf;
     if (s_ok[b]) {
       const u32x4* row = reinterpret_cast<const u32x4*>(k_src + ((size_t)s_src[b] * kPage + t) * D);
-      kx[u] = row[c];
-      ky[u] = row[c + kChunksPerHalf];
+      kx[u] = __builtin_nontemporal_load(row + c);  // the cached segment is read once
+      ky[u] = __builtin_nontemporal_load(row + c + kChunksPerHalf);
     }
   }
   if (v_src != nullptr) {
@@ -78,9 +72,17 @@ __global__ __launch_bounds__(kRelocThreads) void relocate_kernel(
     for (int u = 0; u < kVPerThread; ++u) {
       const int q = tid + u * kRelocThreads;
       const int b = q / (kPage * D / 8), w = q % (kPage * D / 8);
-      if (s_ok[b]) vv[u] = reinterpret_cast<const u32x4*>(v_src + (size_t)s_src[b] * kPage * D)[w];
+      if (s_ok[b]) vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_src + (size_t)s_src[b] * kPage * D) + w);
     }
   }
+  for (int e = tid; e < kMovesPerBatch * kHalf; e += kRelocThreads) {
+    const int b = e / kHalf, j = e % kHalf;
+    double sn = 0.0, cn = 1.0;
+    if (s_ok[b]) sincos((double)s_delta[b] * inv_freq[j], &sn, &cn);
+    cs[b][j][0] = (float)cn;
+    cs[b][j][1] = (float)sn;
+  }
+
   __syncthreads();
 
 #pragma unroll

@@ -200,7 +200,7 @@ int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_meta* meta_hos
  * device, 16-byte aligned, at least importance_workspace_bytes from
  * segkv_plan_sizes (else SEGKV_ERR_WORKSPACE); it receives one partial score
  * per (kv head, key of a block the head's table touches), summed over heads in
- * head order into `importance`. Limits: Hkv <= 256, R <= 65535,
+ * head order into `importance`. Limits: Hkv <= 64, R <= 65535,
  * Hq * (n_last rounded up to 32) <= 4096 (else SEGKV_ERR_UNSUPPORTED).
  */
 int32_t token_importance_topk(const segkv_dims* dims, const segkv_meta* meta_host, const segkv_meta* meta_dev,
