@@ -190,20 +190,23 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
     koff[u] = (row & 15) * D + 8 * (ph ^ k_swz<D>(row));
     voff[u] = (row & 15) * D + 8 * (ph ^ v_swz<D>(row));
   }
+  // The copy of a tile is issued in KLOADS parts spread over the previous
+  // tile's body, so no wave stalls on a burst of vector memory instructions.
+  auto dma_part = [&](uint16_t* kdst, uint16_t* vdst, const uint16_t* kpage, const uint16_t* vpage, int u) {
+    const int blk = wave * KLOADS + u;
+    const uint16_t* ksrc = kpage + koff[u];
+    const uint16_t* vsrc = vpage + voff[u];
+    __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void*)&kdst[blk * 512], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)&vdst[blk * 512], 16, 0, 0);
+  };
+  auto page_of = [&](int t) {  // this wave's page of tile t (wave-uniform), in elements
+    const int pid = __builtin_amdgcn_readfirstlane(spid[kTilePages * (t - t_lo) + wave]);
+    return (size_t)(pid < 0 ? 0 : pid) * kPage * D;
+  };
   auto dma = [&](uint16_t* kdst, uint16_t* vdst, int t) {
-    const int x = kTilePages * (t - t_lo) + wave;
-    const int pid = __builtin_amdgcn_readfirstlane(spid[x]);
-    const size_t page = (size_t)(pid < 0 ? 0 : pid) * kPage * D;  // wave-uniform
-    const uint16_t* kpage = a.k_pool + page;
-    const uint16_t* vpage = a.v_pool + page;
+    const size_t page = page_of(t);
 #pragma unroll
-    for (int u = 0; u < KLOADS; ++u) {
-      const int blk = wave * KLOADS + u;
-      const uint16_t* ksrc = kpage + koff[u];
-      const uint16_t* vsrc = vpage + voff[u];
-      __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void*)&kdst[blk * 512], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)&vdst[blk * 512], 16, 0, 0);
-    }
+    for (int u = 0; u < KLOADS; ++u) dma_part(kdst, vdst, a.k_pool + page, a.v_pool + page, u);
   };
 
   // L2 warm-up of tile t: one 4-byte load per 128-byte line of its K and V
@@ -244,8 +247,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
     constexpr int B = decltype(stage)::value;
     uint16_t* kcur = B ? sk1 : sk0;
     uint16_t* vcur = B ? sv1 : sv0;
-    if (t + 1 < t_hi) dma(B ? sk0 : sk1, B ? sv0 : sv1, t + 1);
-    if (t + 3 < t_hi) touch(t + 3);
+    // copy of tile t+1 (the last tile copies itself again into the idle stage)
+    uint16_t* kn = B ? sk0 : sk1;
+    uint16_t* vn = B ? sv0 : sv1;
+    const size_t npage = page_of(imin(t + 1, t_hi - 1));
+    const uint16_t* knp = a.k_pool + npage;
+    const uint16_t* vnp = a.v_pool + npage;
+    dma_part(kn, vn, knp, vnp, 0);
     const int x0 = kTilePages * (t - t_lo);
     const int p0 = spos[x0], p1 = spos[x0 + 1], p2 = spos[x0 + 2], p3 = spos[x0 + 3];
     const bool all_valid = p0 != INT_MAX && p1 != INT_MAX && p2 != INT_MAX && p3 != INT_MAX;
@@ -264,7 +272,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[kb][i] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int row = 32 * kb + krow0;
@@ -272,6 +280,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
             *reinterpret_cast<const bf16x8*>(&kcur[row * D + 8 * ((2 * ks + lg) ^ k_swz<D>(row))]);
         sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[kb], 0, 0, 0);
       }
+      if (ks == KS / 2 - 1 && KLOADS > 1) dma_part(kn, vn, knp, vnp, 1);
+    }
+    if (KLOADS > 2) dma_part(kn, vn, knp, vnp, 2);
 
     // ---- visibility, only on tiles that straddle a window edge ----
     const int kmin = imin(imin(p0, p1), imin(p2, p3));
@@ -328,6 +339,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
           ls[j & 3] += pv;
         }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+
+    if (KLOADS > 3) dma_part(kn, vn, knp, vnp, 3);
+    static_assert(KLOADS <= 4, "the tile copy is issued in at most four parts");
+    if (t + 3 < t_hi) touch(t + 3);  // issued last: the wait below may leave it in flight
 
     // ---- O^T += V^T P^T (V^T fragments from transpose reads) ----
 #pragma unroll
