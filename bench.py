@@ -141,8 +141,9 @@ def main():
     log(f"visible pairs {pairs} ({flops / 1e9:.2f} GFLOP per attention call)")
     layer = SegPagedLayer(w.num_q_heads, w.num_kv_heads, w.head_dim, w.seg_indptr, w.seg_start, w.seg_len,
                           w.head_class, w.window, w.retr_seg, device=dev)
-    q, k_work, v_work = bf16(w.q), bf16(w.k_work), bf16(w.v_work)
-    k_cache, v_cache = bf16(w.k_cache), bf16(w.v_cache)
+    # V pools are d-major per page ([pages][D][page_size]); the workload holds them token-major
+    q, k_work, v_work = bf16(w.q), bf16(w.k_work), bf16(np.swapaxes(w.v_work, 1, 2))
+    k_cache, v_cache = bf16(w.k_cache), bf16(np.swapaxes(w.v_cache, 1, 2))
     spi, sp = i32(w.seg_page_indptr), i32(w.seg_pages)
     cpi, cp, sos = i32(w.cache_page_indptr), i32(w.cache_pages), i32(w.seg_orig_start)
     T, Hq, D = w.total_q_rows, w.num_q_heads, w.head_dim

@@ -23,6 +23,7 @@
 // a permuted order chosen so each lane ends up holding 8 consecutive keys.
 // Visibility is a per-element predicate evaluated only on tiles that straddle
 // a window edge; other tiles take no mask work at all.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -30,14 +31,17 @@
 namespace segkv {
 namespace {
 
-constexpr int kAttnThreads = 256;
+constexpr int kAttnWaves = 8;                   // waves per attention work-group
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kCombineThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;  // lazy rescale: p <= 2^8 between rescales
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]):
-// wait for vector memory down to 0 / 1 outstanding, leave the other counters alone
+// wait for vector memory down to 0 outstanding, leave the other counters alone
 constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVm1 = 0x0F71;
+// word 3 of a raw buffer resource on gfx9-family parts (32-bit data format)
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 struct AttnArgs {
   const uint16_t* q;
@@ -51,6 +55,7 @@ struct AttnArgs {
   uint16_t* out;
   float* lse;
   char* partials;      // split-KV workspace, partial_slot_bytes(D) per chunk
+  const uint16_t* zero_page;  // device address of g_zero_page
   float scale_log2;  // softmax_scale * log2(e)
   int Hq, G;
 };
@@ -65,64 +70,93 @@ __device__ __forceinline__ int slot_key(int slot) {
 
 constexpr int kMaxItemEntries = kTilePages * kMaxChunkTiles;  // table entries of one item
 
-// LDS of one work-group: two stages of K and V tiles in natural [key][d]
-// layout, whose 16-byte chunks are XOR-swizzled per row so that both operand
-// reads below are free of bank conflicts, plus the item's page table. Every
-// stage is its own __shared__ object and the loop is unrolled by the stage
-// index, so the compiler can tell that reads of one stage do not alias the
-// asynchronous copies into the other and does not wait on those copies.
-template <int D>
-struct StageBufs {
-  uint16_t* k;
-  uint16_t* v;
-};
+// Source of the copies of a missing page: zero K rows (masked by position
+// anyway) and zero V rows, so nothing has to be cleared in LDS. Kernels get its
+// device address through AttnArgs::zero_page.
+__device__ __attribute__((aligned(1024))) uint16_t g_zero_page[kPage * 128] = {};
 
-// (host+device so the device lambdas below may call them)
-template <int D>
-SEGKV_HD int k_swz(int row) { return row % (D / 8); }        // S^T reads: 16 rows, one chunk
-template <int D>
-SEGKV_HD int v_swz(int row) { return (2 * row) % (D / 8); }  // transpose reads: 4 rows, 2 chunks
-
-typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// ds_read_b64_tr_b16 (the builtin exists only in the device compilation pass)
-__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
+// Raw buffer resource over `bytes` bytes at p, and an LDS copy through it:
+// each lane moves 16 (4) bytes from byte voff of the buffer to LDS dst + 16 (4) lane
+// (the builtins exist only in the device compilation pass).
 #if defined(__HIP_DEVICE_COMPILE__)
-  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kBufferRsrcWord3);
+}
+__device__ __forceinline__ void buffer_to_lds16(buf_rsrc rs, void* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void buffer_to_lds4(buf_rsrc rs, void* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 4, voff, 0, 0, 0);
+}
 #else
-  (void)p;
-  return bf16x4{};
+struct buf_rsrc {};
+__device__ inline buf_rsrc make_rsrc(const void*, int) { return {}; }
+__device__ inline void buffer_to_lds16(buf_rsrc, void*, int) {}
+__device__ inline void buffer_to_lds4(buf_rsrc, void*, int) {}
+#endif
+
+// max of x over the two lanes l and l ^ 32 (v_permlane32_swap exchanges the
+// upper half of one register with the lower half of another)
+// (the builtin exists only in the device compilation pass)
+__device__ __forceinline__ float max_halves(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+#else
+  return x;
 #endif
 }
 
-SEGKV_HD int sel4(int i, int a, int b, int c, int d) {
-  return i == 0 ? a : i == 1 ? b : i == 2 ? c : d;
-}
+// LDS of one work-group: two stages of K and V tiles, plus the item's page
+// table. K pages are token-major ([key][d]) with their 16-byte chunks
+// XOR-swizzled per row; V pages are d-major ([d][16 keys], as stored in the
+// pool) with the two 16-byte halves of a row swapped on every other group of
+// 8 rows. Both operand reads below are then free of bank conflicts and full
+// 16-byte reads. Every stage is its own __shared__ object and the loop is
+// unrolled by the stage index, so the compiler can tell that reads of one
+// stage do not alias the asynchronous copies into the other and does not wait
+// on those copies.
 
-// Per item, key tiles t of [t_lo, t_hi) with double-buffered LDS and one
-// barrier per tile: iteration t computes S(t) = K(t) Q^T, the softmax, and
-// O += V(t)^T P(t) from buffer t%2 while K(t+1) and V(t+1) stream straight
-// into the other buffer (global_load_lds, 1 KiB per wave instruction). Two
-// work-groups share a CU, so one wave's softmax overlaps the other's matrix
-// instructions on each SIMD. V^T operands come from LDS transpose reads
-// (ds_read_b64_tr_b16): a 16-lane group whose lanes point at 8-byte runs of 4
-// rows x 16 columns receives the 4-row column slices, so with V kept as
-// [key][d] each lane gets 4 consecutive keys of its own d.
+// (host+device so the device lambdas below may call them)
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) {
-  constexpr int KS = D / 16;            // MFMA k-steps over the head dim
-  constexpr int DB = D / 32;            // 32-wide d blocks of O^T
-  constexpr int KCH = D / 8;            // 16-byte chunks per row
-  constexpr int RPK = 1024 / (2 * D);   // rows per 1 KiB wave transfer
-  constexpr int KLOADS = kTileKeys * KCH / kAttnThreads;  // 1 KiB transfers per wave per tensor
+SEGKV_HD int k_swz(int row) { return row & (D / 8 - 1); }  // S^T reads: 16 rows, one chunk
+
+
+// Per item, key tiles i = 0 .. T-1 (T = t_hi - t_lo, T >= 1) in two LDS
+// stages: K(i) and V(i) live in stage i & 1. The work-group's 8 waves (32 rows
+// each) form two sets with one wave of each on every SIMD (the SIMD id comes
+// from the hardware), which run the same steps one slot apart:
+//   MFMA step of tile i:    S(i) = K(i) Q^T, then O += V(i-1)^T P(i-1)
+//   softmax step of tile i: mask, row max, P(i) = exp2(S(i) - m), l
+// Between two barriers (a slot), set 0 runs the MFMA step of tile s/2 while
+// set 1 runs the softmax step of tile s/2 - 1 (s even), or the softmax step of
+// tile (s-1)/2 while set 1 runs its MFMA step (s odd). Each SIMD's matrix core
+// then works for one of its two waves while the other does vector work. At the
+// start of slot 2i every wave issues its share of the copies of K(i+1) and
+// V(i) into the stages nobody reads any more; they land before the barrier
+// that ends slot 2i+1, ahead of the MFMA step of tile i+1. The V^T operand of
+// a 16-key page is one 16-byte read per lane: 8 consecutive keys of one d.
+template <int D>
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  constexpr int KS = D / 16;                 // MFMA k-steps over the head dim
+  constexpr int DB = D / 32;                 // 32-wide d blocks of O^T
+  constexpr int KCH = D / 8;                 // 16-byte chunks per K row
+  constexpr int RPK = 1024 / (2 * D);        // K rows per 1 KiB transfer
+  constexpr int PLOADS = kPage * KCH / 64;   // 1 KiB transfers per page
+  constexpr int WLOADS = kTilePages * PLOADS / kAttnWaves;  // transfers per wave, tensor and tile
+  static_assert(WLOADS >= 1 && PLOADS % WLOADS == 0, "a wave's copies stay inside one page");
   __shared__ __attribute__((aligned(1024))) uint16_t sk0[kTileKeys * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sk1[kTileKeys * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sk2[kTileKeys * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sv0[kTileKeys * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sv1[kTileKeys * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sv2[kTileKeys * D];
   __shared__ int spid[kMaxItemEntries];
-  __shared__ int spos[kMaxItemEntries];
+  __shared__ __attribute__((aligned(16))) int spos[kMaxItemEntries];
   __shared__ uint32_t swarm[kAttnThreads];  // sink of the L2 warm-up loads
+  __shared__ int s_simd[kAttnWaves];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(a.plan);
   const MTile* mts = reinterpret_cast<const MTile*>(a.plan + a.L.mtiles_off);
@@ -132,7 +166,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
   if (it.mtile < 0) return;  // empty slot of the XCD-aware order
   const MTile mt = mts[it.mtile];
   const int t_lo = chunk_tile_lo(mt.n_tiles, mt.n_chunks, it.chunk);
-  const int t_hi = chunk_tile_lo(mt.n_tiles, mt.n_chunks, it.chunk + 1);
+  const int T = chunk_tile_lo(mt.n_tiles, mt.n_chunks, it.chunk + 1) - t_lo;
+  if (T <= 0) return;  // every m-tile chunk holds a tile (each row sees its own key)
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -153,8 +188,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
   // the item's page table -> LDS (entries past the m-tile's end, or with an
   // invalid page id, become pid -1 / pos INT_MAX)
   const int e_lo = mt.e_begin + kTilePages * t_lo;
-  const int n_ent = kTilePages * (t_hi - t_lo);
-  for (int x = tid; x < n_ent; x += kAttnThreads) {
+  for (int x = tid; x < kTilePages * T; x += kAttnThreads) {
     const int e = e_lo + x;
     int pid = -1, ps = INT_MAX;
     if (e < mt.e_end) {
@@ -168,6 +202,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
     spid[x] = pid;
     spos[x] = ps;
   }
+  // the two waves of each SIMD: the first joins set 0, the second set 1
+  // (hardware register HW_ID, bits 5:4 = SIMD id)
+  const int simd = __builtin_amdgcn_s_getreg(4 | (4 << 6) | (1 << 11));
+  if (lane == 0) s_simd[wave] = simd;
 
   // Q fragments (B operand): Q[row][16 ks + 8 lg + 0..7]
   bf16x8 qf[KS];
@@ -177,100 +215,165 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
   }
   __syncthreads();
+  int rank = 0;
+  for (int w = 0; w < wave; ++w) rank += s_simd[w] == simd;
+  const int set = __builtin_amdgcn_readfirstlane(rank & 1);
 
-  // DMA of tile t into a stage: wave w moves rows [16 w, 16 w + 16) = page w
-  // of the tile, so the page id is wave-uniform. A missing page reads page 0:
-  // its keys are masked by position and its V rows are zeroed before use.
-  // (per-lane element offsets inside the page are fixed: computed once)
-  int koff[KLOADS], voff[KLOADS];
+  // Copies. Transfer g = WLOADS wave + u of a tile moves 1 KiB of page
+  // g / PLOADS, so each wave copies inside one page (wave-uniform page id). A
+  // missing page (id -1) is copied from an all-zero page: its keys are masked
+  // by position and its zero V rows add nothing.
+  int koff[WLOADS], voff[WLOADS];
 #pragma unroll
-  for (int u = 0; u < KLOADS; ++u) {
-    const int row = (wave * KLOADS + u) * RPK + lane / KCH;
-    const int ph = lane % KCH;
-    koff[u] = (row & 15) * D + 8 * (ph ^ k_swz<D>(row));
-    voff[u] = (row & 15) * D + 8 * (ph ^ v_swz<D>(row));
+  for (int u = 0; u < WLOADS; ++u) {
+    const int part = (wave * WLOADS + u) % PLOADS;
+    const int row = part * RPK + lane / KCH;  // K row inside the page
+    koff[u] = row * D + 8 * ((lane % KCH) ^ k_swz<D>(row));
+    // V pages are d-major ([d][16 tokens], 32 bytes per d): 16-byte half hs of
+    // row d lands at hs ^ ((d >> 3) & 1), so the operand reads below (32 rows d,
+    // both halves) hit distinct banks
+    const int c = part * 64 + lane, vd = c >> 1;
+    voff[u] = vd * kPage + 8 * ((c & 1) ^ ((vd >> 3) & 1));
   }
-  // The copy of a tile is issued in KLOADS parts spread over the previous
-  // tile's body, so no wave stalls on a burst of vector memory instructions.
-  auto dma_part = [&](uint16_t* kdst, uint16_t* vdst, const uint16_t* kpage, const uint16_t* vpage, int u) {
-    const int blk = wave * KLOADS + u;
-    const uint16_t* ksrc = kpage + koff[u];
-    const uint16_t* vsrc = vpage + voff[u];
-    __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void*)&kdst[blk * 512], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)&vdst[blk * 512], 16, 0, 0);
+  const int cpage = wave * WLOADS / PLOADS;  // this wave's page of every tile
+  // buffer resource of one page (raw, 4 KiB at D = 128)
+  auto page_rsrc = [&](const uint16_t* page) __attribute__((always_inline)) {
+    return make_rsrc(page, kPage * D * 2);
   };
-  auto page_of = [&](int t) {  // this wave's page of tile t (wave-uniform), in elements
-    const int pid = __builtin_amdgcn_readfirstlane(spid[kTilePages * (t - t_lo) + wave]);
-    return (size_t)(pid < 0 ? 0 : pid) * kPage * D;
-  };
-  auto dma = [&](uint16_t* kdst, uint16_t* vdst, int t) {
-    const size_t page = page_of(t);
+  auto kpage_of = [&](int pid) __attribute__((always_inline)) { return pid < 0 ? a.zero_page : a.k_pool + (size_t)pid * kPage * D; };
+  auto vpage_of = [&](int pid) __attribute__((always_inline)) { return pid < 0 ? a.zero_page : a.v_pool + (size_t)pid * kPage * D; };
+  auto pid_of = [&](int i) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(spid[kTilePages * imin(i, T - 1) + cpage]); };
+  // Copies go through buffer loads (a page-sized buffer resource per source
+  // page): unlike global_load_lds they leave the compiler's LDS-read waits
+  // exact while a copy is in flight.
+  auto copy_k = [&](uint16_t* dst, const uint16_t* page) __attribute__((always_inline)) {
+    const buf_rsrc rs = page_rsrc(page);
 #pragma unroll
-    for (int u = 0; u < KLOADS; ++u) dma_part(kdst, vdst, a.k_pool + page, a.v_pool + page, u);
+    for (int u = 0; u < WLOADS; ++u) buffer_to_lds16(rs, &dst[(wave * WLOADS + u) * 512], 2 * koff[u]);
   };
-
-  // L2 warm-up of tile t: one 4-byte load per 128-byte line of its K and V
-  // pages (256 lines = 256 threads), so that its copy two tiles later hits the
-  // cache. The words land in a scratch LDS area that is never read, so nothing
-  // waits for them until the barrier two tiles on.
-  auto touch = [&](int t) {
-    const int x = kTilePages * (t - t_lo) + ((tid >> 5) & 3);
-    const int pid = spid[x];
-    const uint16_t* base = (tid >> 7) ? a.v_pool : a.k_pool;
-    const uint16_t* src = base + (size_t)(pid < 0 ? 0 : pid) * kPage * D + (size_t)(tid & 31) * (kPage * D / 32);
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&swarm[wave * 64], 4, 0, 0);
+  auto copy_v = [&](uint16_t* dst, const uint16_t* page) __attribute__((always_inline)) {
+    const buf_rsrc rs = page_rsrc(page);
+#pragma unroll
+    for (int u = 0; u < WLOADS; ++u) buffer_to_lds16(rs, &dst[(wave * WLOADS + u) * 512], 2 * voff[u]);
+  };
+  // L2 warm-up of a tile: wave w loads one 4-byte word per 1/64 of the K (w
+  // even) or V (w odd) copy of its page, so that the copy two tiles later hits
+  // the cache. The words land in an LDS area that is never read.
+  const int warm_off = lane * (kPage * D / 32);  // bytes
+  const bool warm_v = (wave & 1) != 0;
+  auto touch = [&](int pid) __attribute__((always_inline)) {
+    buffer_to_lds4(page_rsrc(warm_v ? vpage_of(pid) : kpage_of(pid)), &swarm[wave * 64], warm_off);
   };
 
   // S^T operand: K row this lane feeds for key block 0 (slot permutation; block 1: +32)
   const int krow0 = slot_key(lrow);
-  // V^T operand: this lane's 8-byte run for the transpose reads
-  const int q16 = lane >> 4, bsrc = lane & 15;
-  const int tr_row = 8 * (q16 >> 1) + (bsrc >> 2);         // + 16 kk + 4 half
-  const int tr_chunk = 2 * (q16 & 1) + ((bsrc & 3) >> 1);   // + 4 b
-  const int tr_sub = 4 * (bsrc & 1);                        // element offset inside the chunk
+  // V^T operand: d-major page rows, this lane's row lrow of each 32-row d
+  // block and its 8 keys lg of the page (swizzled half, as written by the copy)
+  const int v_lane = lrow * kPage + 8 * (lg ^ ((lrow >> 3) & 1));
 
   f32x16 o_acc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o_acc[b][i] = 0.f;
+  // The running max m_run is an integer (or -inf), so a rescale factor is an
+  // exact power of two.
   float m_run = -INFINITY, l_run = 0.f;
+  // P of the previous tile in bf16, the B operand of its PV product. The first
+  // MFMA step multiplies these zeros with the zeroed V stage 1.
+  bf16x8 pprev[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pprev[kk][j] = (__bf16)0.f;
+  f32x16 sc[2];   // S(i) from the MFMA step to the softmax step
+  int4 tpos_v;    // key positions of tile i's pages (read in its MFMA step)
+  // a rescale of O found due by a softmax step, applied before the next PV product
+  float o_scale = 1.f;
+  bool o_scale_due = false;
 
-  dma(sk0, sv0, t_lo);
-  if (t_lo + 1 < t_hi) touch(t_lo + 1);
-  if (t_lo + 2 < t_hi) touch(t_lo + 2);
+  // stage buffers of tile i (stage i % 3, a compile-time index)
+  auto kst = [&](auto st) __attribute__((always_inline)) {
+    constexpr int S = decltype(st)::value % 3;
+    return S == 0 ? sk0 : S == 1 ? sk1 : sk2;
+  };
+  auto vst = [&](auto st) __attribute__((always_inline)) {
+    constexpr int S = decltype(st)::value % 3;
+    return S == 0 ? sv0 : S == 1 ? sv1 : sv2;
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+
+  // K(0), K(1), V(0) before the loop; V(-1) (stage 2) is zero; page ids of
+  // this wave's page in tiles i+1 .. i+4 (wave-uniform, clamped to T-1)
+  int pid1 = pid_of(1), pid2 = pid_of(2), pid3 = pid_of(3), pid4 = pid_of(4);
+  {
+    const int pid0 = pid_of(0);
+    copy_k(sk0, kpage_of(pid0));
+    copy_k(sk1, kpage_of(pid1));
+    copy_v(sv0, vpage_of(pid0));
+  }
+  for (int e = tid * 8; e < kTileKeys * D; e += kAttnThreads * 8) *reinterpret_cast<u32x4*>(&sv2[e]) = u32x4{0, 0, 0, 0};
+  touch(pid2);
+  touch(pid3);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // one tile; stage B holds tile t, stage B^1 receives tile t+1
-  auto body = [&](auto stage, int t) {
-    constexpr int B = decltype(stage)::value;
-    uint16_t* kcur = B ? sk1 : sk0;
-    uint16_t* vcur = B ? sv1 : sv0;
-    // copy of tile t+1 (the last tile copies itself again into the idle stage)
-    uint16_t* kn = B ? sk0 : sk1;
-    uint16_t* vn = B ? sv0 : sv1;
-    const size_t npage = page_of(imin(t + 1, t_hi - 1));
-    const uint16_t* knp = a.k_pool + npage;
-    const uint16_t* vnp = a.v_pool + npage;
-    dma_part(kn, vn, knp, vnp, 0);
-    const int x0 = kTilePages * (t - t_lo);
-    const int p0 = spos[x0], p1 = spos[x0 + 1], p2 = spos[x0 + 2], p3 = spos[x0 + 3];
-    const bool all_valid = p0 != INT_MAX && p1 != INT_MAX && p2 != INT_MAX && p3 != INT_MAX;
-    if (!all_valid) {  // zero V rows of missing pages (0 * NaN would poison O); rare, block-uniform
-      const int pg = tid >> 6;  // 4 pages x 64 threads, 16 rows x D per page
-      if (sel4(pg, p0, p1, p2, p3) == INT_MAX)
-        for (int e = (tid & 63) * 8; e < kPage * D; e += 64 * 8)
-          *reinterpret_cast<u32x4*>(&vcur[pg * kPage * D + e]) = u32x4{0, 0, 0, 0};
-      __syncthreads();
+  auto bar = [&]() __attribute__((always_inline)) {  // bare barrier; the empty asm statements keep LDS accesses on their side
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // at the end of slot 2i+1: this wave's copies of slot 2i-2 have landed (those
+  // of slot 2i, kCopyOps vector memory operations, may stay in flight; vector
+  // memory completes in order), then a barrier
+  constexpr int kCopyOps = 2 * WLOADS + 1;
+  static_assert(kCopyOps < 16, "vmcnt immediate");
+  auto wait_copies_bar = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kCopyOps);
+    bar();
+  };
+  // copies of slot 2i: K(i+2) (near the end the last tile's K again, into an
+  // idle stage) and V(i+1), then the warm-up of tile i+4; next page id lookup
+  auto copies = [&](uint16_t* kdst, uint16_t* vdst, int i) __attribute__((always_inline)) {
+    copy_k(kdst, kpage_of(pid2));
+    copy_v(vdst, vpage_of(pid1));
+    touch(pid4);
+    pid1 = pid2;
+    pid2 = pid3;
+    pid3 = pid4;
+    pid4 = pid_of(i + 5);
+  };
+  auto rescale_o = [&]() __attribute__((always_inline)) {
+    if (o_scale_due) {
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o_acc[b][i] *= o_scale;
+      o_scale_due = false;
     }
+  };
+  // PV piece of page kk: O^T[b] += V^T(page kk) P^T(page kk) for every d block
+  auto pv_page = [&](const uint16_t* vbuf, const bf16x8& pk, int kk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vbuf[(kk * D + 32 * b) * kPage + v_lane]);
+      o_acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk, o_acc[b], 0, 0, 0);
+    }
+  };
 
-    // ---- S^T = K Q^T ----
-    f32x16 sc[2];
+  // MFMA step of tile i (stage P = i % 3): S(i) = K(i) Q^T, O += V(i-1)^T P(i-1)
+  auto mfma_step = [&](auto par, int i) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    const uint16_t* kcur = kst(par);
+    const uint16_t* vprev = vst(std::integral_constant<int, P + 2>{});
+    tpos_v = *reinterpret_cast<const int4*>(&spos[kTilePages * i]);
+    rescale_o();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sc[kb][i] = 0.f;
+      for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
@@ -280,30 +383,47 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
             *reinterpret_cast<const bf16x8*>(&kcur[row * D + 8 * ((2 * ks + lg) ^ k_swz<D>(row))]);
         sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[kb], 0, 0, 0);
       }
-      if (ks == KS / 2 - 1 && KLOADS > 1) dma_part(kn, vn, knp, vnp, 1);
     }
-    if (KLOADS > 2) dma_part(kn, vn, knp, vnp, 2);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) pv_page(vprev, pprev[kk], kk);
+    // schedule: keep kAhead operand reads in flight ahead of the matrix
+    // instructions (each read is one MFMA's A operand), so that LDS latency
+    // hides behind the MFMA pipeline
+    constexpr int kOps = 2 * KS + 4 * DB, kAhead = 10;
+    if (kAhead > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // DS reads
+#pragma unroll
+    for (int m = 0; m < kOps - kAhead; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+    }
+  };
 
-    // ---- visibility, only on tiles that straddle a window edge ----
+  // softmax step of tile i: visibility, row max (lazy rescale: the running max
+  // moves only when a tile's max exceeds it by more than 2^8, and then to the
+  // integer above), P(i) in bf16 and the row sums
+  auto softmax_step = [&]() __attribute__((always_inline)) {
+    const int p0 = __builtin_amdgcn_readfirstlane(tpos_v.x), p1 = __builtin_amdgcn_readfirstlane(tpos_v.y);
+    const int p2 = __builtin_amdgcn_readfirstlane(tpos_v.z), p3 = __builtin_amdgcn_readfirstlane(tpos_v.w);
+    const bool all_valid = p0 != INT_MAX && p1 != INT_MAX && p2 != INT_MAX && p3 != INT_MAX;
     const int kmin = imin(imin(p0, p1), imin(p2, p3));
     const int kmax = imax(imax(p0 == INT_MAX ? 0 : p0, p1 == INT_MAX ? 0 : p1),
                           imax(p2 == INT_MAX ? 0 : p2, p3 == INT_MAX ? 0 : p3)) + kPage - 1;
     const bool full = all_valid && kmax <= pos_min && (!is_local || kmin >= lo_max);
-    if (!full) {
+    if (!full) {  // only tiles that straddle a window edge
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int pp = 2 * kb + (i >> 3);
+        for (int e = 0; e < 16; ++e) {
+          const int pp = 2 * kb + (e >> 3);
           const int ps = pp == 0 ? p0 : pp == 1 ? p1 : pp == 2 ? p2 : p3;
-          const int j = ps + 8 * lg + (i & 7);
+          const int j = ps + 8 * lg + (e & 7);
           const bool vis = ps != INT_MAX && j <= pos && j >= lo_row;
-          sc[kb][i] = vis ? sc[kb][i] : -INFINITY;
+          sc[kb][e] = vis ? sc[kb][e] : -INFINITY;
         }
     }
-
-    // ---- online softmax (lazy rescale: only when the max grows by > 2^8) ----
-    // row max as a 4-way tree of 3-input maxima (short dependency chains)
     float tm[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -312,71 +432,74 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
       tm[c] = fmaxf(fmaxf(fmaxf(v[o], v[o + 1]), fmaxf(v[o + 2], v[o + 3])),
                     fmaxf(fmaxf(v[o + 4], v[o + 5]), fmaxf(v[o + 6], v[o + 7])));
     }
-    float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float tmax = max_halves(fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3])));
     const float m_tile = tmax * a.scale_log2;
-    const bool rescale = m_tile > m_run + kRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
-      const float alpha = rescale ? exp2f(m_run - m_tile) : 1.f;  // m_run = -inf -> 0
-      l_run *= alpha;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o_acc[b][i] *= alpha;
-      m_run = rescale ? m_tile : m_run;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    bf16x8 pf[4];
+    const bool grow = m_tile > m_run + kRescaleThreshold;
+    const float m_new = grow ? ceilf(m_tile) : m_run;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
     float ls[4] = {0.f, 0.f, 0.f, 0.f};  // four partial row sums (short dependency chains)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hh + j], a.scale_log2, -m_use));
-          pf[2 * kb + hh][j] = (__bf16)pv;
-          ls[j & 3] += pv;
-        }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-
-    if (KLOADS > 3) dma_part(kn, vn, knp, vnp, 3);
-    static_assert(KLOADS <= 4, "the tile copy is issued in at most four parts");
-    if (t + 3 < t_hi) touch(t + 3);  // issued last: the wait below may leave it in flight
-
-    // ---- O^T += V^T P^T (V^T fragments from transpose reads) ----
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        bf16x4 v4[2];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int row = 16 * kk + tr_row + 4 * half;
-          const int ch = 4 * b + tr_chunk;
-          const uint16_t* src = &vcur[row * D + 8 * (ch ^ v_swz<D>(row)) + tr_sub];
-          v4[half] = lds_read_tr16(src);
-        }
-        const bf16x8 vf = {v4[0][0], v4[0][1], v4[0][2], v4[0][3], v4[1][0], v4[1][1], v4[1][2], v4[1][3]};
-        o_acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o_acc[b], 0, 0, 0);
+      for (int j = 0; j < 8; ++j) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sc[kk >> 1][8 * (kk & 1) + j], a.scale_log2, -m_use));
+        pprev[kk][j] = (__bf16)pv;
+        ls[j & 3] += pv;
       }
-
-    // this wave's copy of tile t+1 has landed (only the warm-up load issued
-    // after it may still be in flight; vector memory completes in order), then
-    // a bare barrier: the workgroup fence of __syncthreads would also wait for
-    // the warm-up. The empty asm statements keep the compiler from moving LDS
-    // accesses across it.
-    if (t + 3 < t_hi)
-      __builtin_amdgcn_s_waitcnt(kWaitVm1);
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    // l moves to the new max now; O before the next PV product
+    const float alpha = grow ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(m_run - ceilf(m_tile)))) : 1.f;
+    l_run = l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
+    m_run = m_new;
+    o_scale = alpha;
+    o_scale_due = __builtin_amdgcn_ballot_w64(grow) != 0;
   };
-  for (int t = t_lo; t < t_hi; t += 2) {
-    body(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < t_hi) body(std::integral_constant<int, 1>{}, t + 1);
+
+  if (set == 0) {
+    // slot 2i: copies + MFMA step of tile i; slot 2i+1: softmax step of tile i
+    auto tile = [&](auto par, int i) __attribute__((always_inline)) {
+      constexpr int P = decltype(par)::value;
+      copies(kst(std::integral_constant<int, P + 2>{}), vst(std::integral_constant<int, P + 1>{}), i);
+      mfma_step(par, i);
+      bar();
+      softmax_step();
+      wait_copies_bar();
+    };
+    for (int i = 0; i < T; i += 3) {
+      tile(S0{}, i);
+      if (i + 1 < T) tile(S1{}, i + 1);
+      if (i + 2 < T) tile(S2{}, i + 2);
+    }
+  } else {
+    // slot 0: copies of tile 0; then slot 2i+1: MFMA step of tile i; slot
+    // 2i+2: copies of tile i+1 + softmax step of tile i
+    copies(sk2, sv1, 0);
+    bar();
+    auto tile = [&](auto par, int i) __attribute__((always_inline)) {
+      constexpr int P = decltype(par)::value;
+      mfma_step(par, i);
+      wait_copies_bar();
+      if (i + 1 < T) {
+        copies(kst(std::integral_constant<int, P + 3>{}), vst(std::integral_constant<int, P + 2>{}), i + 1);
+        softmax_step();
+        bar();
+      } else {
+        softmax_step();
+      }
+    };
+    for (int i = 0; i < T; i += 3) {
+      tile(S0{}, i);
+      if (i + 1 < T) tile(S1{}, i + 1);
+      if (i + 2 < T) tile(S2{}, i + 2);
+    }
+  }
+  // the last copies and warm-up loads land before the work-group may end
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  {  // the last tile's PV product: V(T-1) sits in stage (T-1) % 3, landed before the last barrier
+    rescale_o();
+    const int last = (T - 1) % 3;
+    const uint16_t* vlast = last == 0 ? sv0 : last == 1 ? sv1 : sv2;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) pv_page(vlast, pprev[kk], kk);
   }
 
   const float l_row = l_run + __shfl_xor(l_run, 32);
@@ -419,9 +542,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_main_kernel(AttnArgs a) 
 //   O = sum_c 2^(m_c - m*) l_c (O_c / l_c) / sum_c 2^(m_c - m*) l_c,
 //   LSE = (m* + log2 sum_c 2^(m_c - m*) l_c) ln 2.
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs a) {
   constexpr int DG = D / 4;                       // 4-element groups per row
-  constexpr int kRowsPerBlock = kAttnThreads / DG;
+  constexpr int kRowsPerBlock = kCombineThreads / DG;
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(a.plan);
   if ((int)blockIdx.x >= hdr->n_split) return;
   const MTile* mts = reinterpret_cast<const MTile*>(a.plan + a.L.mtiles_off);
@@ -479,6 +602,30 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) 
   if (dg == 0 && a.lse != nullptr) a.lse[(size_t)qrow * a.Hq + qhead] = (mstar + log2f(lsum)) * kLn2;
 }
 
+// Device address of g_zero_page on the current device, looked up once per
+// device (the symbol's host-side name is not a device address).
+constexpr int kMaxDevices = 64;
+
+const uint16_t* zero_page_address() {
+  static std::mutex mu;
+  static const uint16_t* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_zero_page)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    addr[dev] = static_cast<const uint16_t*>(p);
+  }
+  return addr[dev];
+}
+
 }  // namespace
 }  // namespace segkv
 
@@ -520,6 +667,8 @@ extern "C" int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_met
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.partials = static_cast<char*>(workspace);
+  a.zero_page = zero_page_address();
+  if (a.zero_page == nullptr) return fail(SEGKV_ERR_HIP, "hipGetSymbolAddress of the zero page failed");
   a.scale_log2 = softmax_scale * kLog2e;
   a.Hq = dims->num_q_heads;
   a.G = dims->num_q_heads / dims->num_kv_heads;
@@ -527,11 +676,11 @@ extern "C" int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_met
   if (dims->head_dim == 128) {
     attn_main_kernel<128><<<hp.n_items, kAttnThreads, 0, s>>>(a);
     SEGKV_LAUNCH_CHECK();
-    if (hp.n_split > 0) attn_combine_kernel<128><<<dim3(hp.n_split, kMRows * 32 / kAttnThreads), kAttnThreads, 0, s>>>(a);
+    if (hp.n_split > 0) attn_combine_kernel<128><<<dim3(hp.n_split, kMRows * 32 / kCombineThreads), kCombineThreads, 0, s>>>(a);
   } else {
     attn_main_kernel<64><<<hp.n_items, kAttnThreads, 0, s>>>(a);
     SEGKV_LAUNCH_CHECK();
-    if (hp.n_split > 0) attn_combine_kernel<64><<<dim3(hp.n_split, kMRows * 16 / kAttnThreads), kAttnThreads, 0, s>>>(a);
+    if (hp.n_split > 0) attn_combine_kernel<64><<<dim3(hp.n_split, kMRows * 16 / kCombineThreads), kCombineThreads, 0, s>>>(a);
   }
   SEGKV_LAUNCH_CHECK();
   return SEGKV_OK;

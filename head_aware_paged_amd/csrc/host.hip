@@ -36,7 +36,7 @@ int32_t validate_layout(const segkv_dims* d, const segkv_meta* m) {
   REQUIRE(d->head_dim == 64 || d->head_dim == 128, SEGKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   REQUIRE(d->page_size == kPage, SEGKV_ERR_UNSUPPORTED, "page_size must be 16");
   const int G = d->num_q_heads / d->num_kv_heads;
-  REQUIRE(G <= kMRows && kMRows % G == 0, SEGKV_ERR_UNSUPPORTED, "group size Hq/Hkv must divide 128");
+  REQUIRE(G <= kMRows && kMRows % G == 0, SEGKV_ERR_UNSUPPORTED, "group size Hq/Hkv must divide 256");
   REQUIRE(m->seg_indptr && m->seg_start && m->seg_len && m->head_class && m->window && m->retr_seg,
           SEGKV_ERR_INVALID_ARG, "a metadata array is NULL");
   const int R = d->num_requests, S = d->num_segments, Hkv = d->num_kv_heads;
@@ -93,7 +93,7 @@ HeadView head_view_host(const segkv_dims& d, const segkv_meta& m, int r, int h) 
 }
 
 int attention_slots() {
-  // Resident attention work-groups: 2 per CU (launch bounds 256 threads, 2 WG/CU).
+  // Resident attention work-groups: 1 per CU (512 threads, two waves per SIMD).
   static std::once_flag once;
   static int cus = 256;
   std::call_once(once, [] {
@@ -103,7 +103,7 @@ int attention_slots() {
       cus = n;
     (void)hipGetLastError();
   });
-  return cus * 2;
+  return cus;
 }
 
 // Greedy longest-processing-time schedule of `sizes` on `bins` identical slots.

@@ -26,7 +26,7 @@ namespace segkv {
 constexpr int kPage = 16;          // tokens per page
 constexpr int kTilePages = 4;      // pages per attention key tile
 constexpr int kTileKeys = kPage * kTilePages;
-constexpr int kMRows = 128;        // query rows per attention work-group (G heads x 128/G positions)
+constexpr int kMRows = 256;        // query rows per attention work-group (G heads x 256/G positions)
 constexpr int kMaxChunkTiles = 256;  // key tiles per work item (its page table is staged in LDS)
 constexpr int kClassGlobal = 0, kClassLocal = 1, kClassRetrieval = 2, kClassDense = 3;
 

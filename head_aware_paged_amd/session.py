@@ -74,6 +74,7 @@ class SegPagedLayer:
                       self.num_moves, self.dims.page_size, self.dims.head_dim, rope_theta, stream=stream)
 
     def attention(self, q, k_pool, v_pool, out=None, lse=None, want_lse=True, stream=None):
+        """k_pool: [pages][page_size][head_dim] bf16; v_pool: [pages][head_dim][page_size] bf16 (d-major)."""
         T, Hq = int(self.sizes["total_q_rows"]), self.dims.num_q_heads
         if out is None:
             out = torch.empty(T, Hq, self.dims.head_dim, dtype=torch.bfloat16, device=self.device)

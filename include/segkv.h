@@ -152,8 +152,9 @@ int32_t segkv_visible_spans(const segkv_dims* dims, const segkv_meta* meta_host,
  * dst_page[m] of v_dst = copy of V page src_page[m] of v_src.
  * Rotation: rotate-half pairs (j, j + D/2), angle delta * theta^(-2j/D);
  * cos/sin from fp64, products in fp32, result rounded to bf16 (RNE).
- * Pools: [pages][page_size][head_dim] bf16, k_src/v_src with src_pool_pages
- * pages and k_dst/v_dst with dst_pool_pages pages. Moves with a page id out of
+ * Pools: K [pages][page_size][head_dim] bf16 (token-major), V [pages][head_dim]
+ * [page_size] bf16 (d-major); k_src/v_src with src_pool_pages pages and
+ * k_dst/v_dst with dst_pool_pages pages. V pages are copied verbatim. Moves with a page id out of
  * range are skipped. In place (src page == dst page, same pool) is allowed;
  * otherwise destinations must not overlap sources.
  */
@@ -172,8 +173,10 @@ int32_t rope_relocate(const void* k_src, void* k_dst, const void* v_src, void* v
  * lse: [T_q][Hq] fp32 natural-log sum of exp(scale * q k) over visible keys
  *      (nullable).
  * Keys are read only through the page tables written by segkv_build_pages for
- * the same layout, whose plan must be passed in `plan`. k_pool/v_pool:
- * [pool_pages][P][D] bf16. workspace: attn_workspace_bytes from
+ * the same layout, whose plan must be passed in `plan`. k_pool: [pool_pages]
+ * [P][D] bf16, token-major; v_pool: [pool_pages][D][P] bf16, d-major (element
+ * (d, t) of a page at d * P + t), so that the V^T operand of the PV product
+ * is 8 consecutive tokens of one d. workspace: attn_workspace_bytes from
  * segkv_plan_sizes (may be NULL when that is 0).
  */
 int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_meta* meta_host,

@@ -15,6 +15,12 @@ def bf16(u16) -> torch.Tensor:
     return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
 
 
+def v_pages(u16) -> np.ndarray:
+    """A V pool [pages][P][D] (token-major, as the workloads hold it) in the
+    library's d-major page layout [pages][D][P]."""
+    return np.ascontiguousarray(np.swapaxes(u16, 1, 2))
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
@@ -34,12 +40,12 @@ class Dev:
     def __init__(self, w, cache=True):
         self.q = bf16(w.q)
         self.k_work = bf16(w.k_work)
-        self.v_work = bf16(w.v_work)
+        self.v_work = bf16(v_pages(w.v_work))
         self.seg_page_indptr = i32(w.seg_page_indptr)
         self.seg_pages = i32(w.seg_pages)
         if cache and w.k_cache.shape[0] > 0:
             self.k_cache = bf16(w.k_cache)
-            self.v_cache = bf16(w.v_cache)
+            self.v_cache = bf16(v_pages(w.v_cache))
             self.cache_page_indptr = i32(w.cache_page_indptr)
             self.cache_pages = i32(w.cache_pages)
             self.seg_orig_start = i32(w.seg_orig_start)

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import Dev, assert_attn_close, bf16, bits, build, sample_rows
+from gpu_util import Dev, assert_attn_close, bf16, bits, build, sample_rows, v_pages
 
 pytestmark = pytest.mark.gpu
 
@@ -110,7 +110,7 @@ def test_pages_outside_tables_are_never_read(name):
     wk[unused] = 0x7FC0
     wv[unused] = 0x7FC0
     dev = Dev(w)
-    dev.k_work, dev.v_work = bf16(wk), bf16(wv)
+    dev.k_work, dev.v_work = bf16(wk), bf16(v_pages(wv))
     ob2, lse2, _, _ = run_attn(w, dev)
     assert np.all(np.isfinite(oracle.bf16_bits_to_f64(ob2)))
     assert np.array_equal(ob2, ob) and np.array_equal(lse2, lse)
@@ -149,6 +149,50 @@ def test_sentinel_keys_at_window_edges():
     ob, lse, _, _ = run_attn(w)
     O, L = oracle.attention(w)
     assert_attn_close(ob, lse, O, L, name="sentinels")
+
+
+def _plant_aligned_key(w, r, h, j, qvec, score):
+    """Key j of (request r, kv head h) := a multiple of qvec whose scaled score
+    against qvec is `score`; its V row := 0.5."""
+    P, Hkv, D = w.page_size, w.num_kv_heads, w.head_dim
+    for s in w.segments_of(r):
+        b = int(w.seg_start[s])
+        if b <= j < b + int(w.seg_len[s]):
+            pid = w.seg_pages[w.seg_page_indptr[s * Hkv + h] + (j - b) // P]
+            alpha = score * np.sqrt(D) / float(qvec @ qvec)
+            w.k_work[pid, (j - b) % P] = oracle.f64_to_bf16_bits(alpha * qvec)
+            w.v_work[pid, (j - b) % P] = oracle.f64_to_bf16_bits(np.full(D, 0.5))
+            return
+    raise AssertionError((r, h, j))
+
+
+@pytest.mark.parametrize("score", [35.0, 100.0])
+@pytest.mark.parametrize("name", ["g4_d128_q512", "ragged_g8"])
+def test_late_score_jump(name, score):
+    # A key near the end of a row's visible range whose score stands `score`
+    # above the row's typical scores (which are O(1)): 35 stays within the
+    # growth a single pass allows over the row's first running max, 100 (about
+    # 2^140 in probability) exceeds it and takes the exact-max pass. Both must
+    # match the oracle, and nothing may overflow.
+    w = small(name)
+    print(f"case {w.name}: late score jump {score}", flush=True)
+    G = w.num_q_heads // w.num_kv_heads
+    for r in range(w.num_requests):
+        bq = int(w.seg_start[w.query_segment(r)])
+        Lq = int(w.cu_q[r + 1] - w.cu_q[r])
+        for t in sorted({Lq - 1, Lq // 2}):
+            i, row = bq + t, int(w.cu_q[r]) + t
+            for h in range(w.num_kv_heads):
+                ivs = oracle.visible_intervals(w, r, h, i)
+                cached = [hi - 1 for lo, hi in ivs if hi - 1 < bq] + [bq - 1 for lo, hi in ivs if lo < bq <= hi - 1]
+                j = max(cached) if cached else i - 1
+                if j < 0:
+                    continue
+                _plant_aligned_key(w, r, h, j, oracle.bf16_bits_to_f64(w.q[row, h * G]), score)
+    ob, lse, _, _ = run_attn(w)
+    assert np.all(np.isfinite(oracle.bf16_bits_to_f64(ob))) and np.all(np.isfinite(lse))
+    O, L = oracle.attention(w)
+    assert_attn_close(ob, lse, O, L, name=f"{w.name}+jump{score:g}")
 
 
 @pytest.mark.parametrize("name", ["mistral7b_32k", "qwen3_32b_varlen", "long_64k"])
