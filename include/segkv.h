@@ -26,7 +26,7 @@
  *    absolute positions within a request.
  *  - Identical inputs give bitwise-identical outputs (no float atomics).
  *  - Supported: head_dim 64 or 128, page_size 16, num_q_heads a multiple of
- *    num_kv_heads with group size G = Hq/Hkv dividing 128.
+ *    num_kv_heads with group size G = Hq/Hkv dividing 256.
  */
 #ifndef SEGKV_H_
 #define SEGKV_H_
