@@ -8,21 +8,25 @@
 // a key by delta positions rotates pair (j, j + D/2) by delta * omega_j.
 //
 // Bandwidth-bound: every move reads and writes one K page (and one V page).
-// A work-group takes 8 moves, keeps all 16-byte loads of the batch in flight,
-// and shares the batch's cos/sin table (fp64 sincos, rounded to fp32) in LDS.
+// A work-group takes a batch of 1 (D = 128) or 2 (D = 64) moves, so that a
+// layer's few thousand moves spread over many work-groups per CU; it keeps all
+// 16-byte loads of the batch in flight and computes the batch's cos/sin table
+// (fp64 sincos, rounded to fp32, in LDS) while they fly.
 #include "common.h"
 
 namespace segkv {
 namespace {
 
-constexpr int kRelocThreads = 256;
-constexpr int kMovesPerBatch = 8;
+constexpr int kRelocThreads = 128;
+template <int D>
+constexpr int moves_per_batch() { return D == 128 ? 1 : 2; }
 
 template <int D>
 __global__ __launch_bounds__(kRelocThreads) void relocate_kernel(
     const uint16_t* __restrict__ k_src, uint16_t* __restrict__ k_dst, const uint16_t* __restrict__ v_src,
     uint16_t* __restrict__ v_dst, int64_t src_pages, int64_t dst_pages, const int32_t* __restrict__ src_page,
     const int32_t* __restrict__ dst_page, const int32_t* __restrict__ delta, int n_moves, double theta) {
+  constexpr int kMovesPerBatch = moves_per_batch<D>();
   constexpr int kHalf = D / 2;
   constexpr int kChunksPerHalf = kHalf / 8;          // 16-byte chunks in one half row
   constexpr int kPairsPerPage = kPage * kChunksPerHalf;
@@ -38,7 +42,6 @@ __global__ __launch_bounds__(kRelocThreads) void relocate_kernel(
 
   const int tid = threadIdx.x;
   const int m0 = blockIdx.x * kMovesPerBatch;
-  if (tid < kHalf) inv_freq[tid] = pow(theta, -2.0 * (double)tid / (double)D);
   if (tid < kMovesPerBatch) {
     const int m = m0 + tid;
     int s = -1, d = -1, ok = 0, dl = 0;
@@ -75,6 +78,8 @@ __global__ __launch_bounds__(kRelocThreads) void relocate_kernel(
       if (s_ok[b]) vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_src + (size_t)s_src[b] * kPage * D) + w);
     }
   }
+  if (tid < kHalf) inv_freq[tid] = pow(theta, -2.0 * (double)tid / (double)D);
+  __syncthreads();
   for (int e = tid; e < kMovesPerBatch * kHalf; e += kRelocThreads) {
     const int b = e / kHalf, j = e % kHalf;
     double sn = 0.0, cn = 1.0;
@@ -145,7 +150,7 @@ extern "C" int32_t rope_relocate(const void* k_src, void* k_dst, const void* v_s
     return fail(SEGKV_ERR_INVALID_ARG, "v_src and v_dst must both be given or both be NULL");
   if (!aligned16(k_src) || !aligned16(k_dst) || (v_src && (!aligned16(v_src) || !aligned16(v_dst))))
     return fail(SEGKV_ERR_ALIGNMENT, "pools must be 16-byte aligned");
-  const int grid = cdiv(n_moves, kMovesPerBatch);
+  const int grid = cdiv(n_moves, head_dim == 128 ? moves_per_batch<128>() : moves_per_batch<64>());
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto ks = static_cast<const uint16_t*>(k_src);
   auto kd = static_cast<uint16_t*>(k_dst);
