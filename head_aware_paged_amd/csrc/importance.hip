@@ -15,6 +15,8 @@
 // Top-k: radix select (4 passes of 8 bits) on the fp32 bit patterns, which
 // order like the values for non-negative scores, then one ordered compaction:
 // every key above the threshold plus the lowest-indexed keys equal to it.
+#include <type_traits>
+
 #include "common.h"
 
 namespace segkv {
@@ -240,15 +242,25 @@ __global__ __launch_bounds__(256) void importance_reduce_kernel(const char* __re
 // One 1024-thread work-group selects the top k of one score vector. Wave w
 // owns the contiguous key range [256 S w, 256 S (w + 1)); inside it, sub-block
 // u holds keys 256 u + 4 lane + e (e < 4), kept in registers for every pass.
-// Four 8-bit digit passes find the k-th largest key; each pass counts the
-// candidates' digits in 64 lane-private LDS histograms (bin b of lane l at
-// 64 b + l, so a wave's increments never share a bank or an address) and
-// picks the digit with a suffix scan. One ordered compaction then writes
-// every key above the threshold and the lowest-indexed keys equal to it.
+// Up to four 8-bit digit passes find the k-th largest key. Each pass counts
+// the candidates' digits in 64 lane-private LDS histograms (bin b of lane l at
+// 64 b + l, so a wave's increments never share a bank or an address). Every
+// wave then sums the copies of 16 bins, and after one barrier every wave
+// scans the 256 bin totals itself, so the chosen digit needs no broadcast.
+// Two histogram buffers alternate: the one just summed is cleared while the
+// next pass counts into the other. The passes stop as soon as every key
+// sharing the chosen digits is needed; the threshold is then those digits
+// with zero low bits. One ordered compaction writes every key above the
+// threshold and the lowest-indexed keys equal to it.
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kTopkSub = 256;  // keys per wave sub-block (64 lanes x 4)
 constexpr int kTopkMaxRegSub = 15;  // register-resident up to 15 x 256 x 16 = 61440 keys (no spills)
+constexpr int kTopkHist = 256 * 64;  // words of one histogram buffer
+constexpr int kTopkSegSub = 9;       // up to 9 sub-blocks per wave, every wave's selection fits its own LDS segment
+constexpr int kTopkLdsWords = kTopkWaves * kTopkSub * kTopkSegSub + 64;  // >= both histogram buffers
+constexpr int kTopkStageMax = kTopkLdsWords - 64;  // staged output indices; the last 64 words take unselected writes
+static_assert(kTopkStageMax >= 2 * kTopkHist, "the LDS array must hold both histogram buffers");
 
 // fp32 bit pattern -> unsigned integer of the same order (-0 ranks as +0)
 __device__ __forceinline__ uint32_t ordered_bits(uint32_t b) {
@@ -275,8 +287,9 @@ __device__ __forceinline__ u32x4 topk_load4(const uint32_t* bits, int j, int n, 
   return o;
 }
 
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+// Lanes below this one whose bit is set in m, plus acc.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m, uint32_t acc) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, acc));
 }
 
 // S > 0: S sub-blocks per wave held in registers; S == 0: ns_rt sub-blocks
@@ -285,7 +298,8 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Wpass-failed"
 // DPP moves inside rows of 16 lanes; a lane whose source lies outside its row reads 0
-constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppRowShl4 = 0x104, kDppRowShl8 = 0x108;
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E;
+constexpr int kDppRowShl1 = 0x101, kDppRowShl2 = 0x102, kDppRowShl4 = 0x104, kDppRowShl8 = 0x108;
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
@@ -294,9 +308,8 @@ __device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
 template <int S>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
                                                             int32_t* __restrict__ idx_out, int n, int k, int ns_rt) {
-  __shared__ uint32_t hist[256 * 64];  // reused to stage the output indices when k <= 16384
-  __shared__ uint32_t s_wsum[kTopkWaves];
-  __shared__ uint32_t s_sel[3];
+  __shared__ uint32_t hist[kTopkLdsWords];  // two histogram buffers; afterwards the staged output
+  __shared__ u32x4 s_bins[64];              // bin totals of the current pass
   __shared__ int s_tot[kTopkWaves][2];
   constexpr int SR = S > 0 ? S : 1;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -311,158 +324,237 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   }
 #define SEGKV_TOPK_KEYS(u) (S > 0 ? reg[(S > 0 ? (u) : 0)] : topk_load4(bits, base + kTopkSub * (u), n, vec))
 
-  for (int x = tid; x < 256 * 64 / 4; x += kTopkThreads) reinterpret_cast<u32x4*>(hist)[x] = u32x4{0, 0, 0, 0};
+  // Byte address of a key's counter in buffer bf: byte 0 = 4 lane, byte 1 =
+  // the digit (byte 3 - pass of the key), byte 2 = the buffer; one v_perm.
+  const uint32_t lane4 = 4u * (uint32_t)lane;
+  char* const hbytes = reinterpret_cast<char*>(hist);
+#pragma unroll
+  for (int x = tid; x < 2 * kTopkHist / 4; x += kTopkThreads) reinterpret_cast<u32x4*>(hist)[x] = u32x4{0, 0, 0, 0};
   __syncthreads();
+#pragma unroll
+  for (int u = 0; u < (S > 0 ? S : ns); ++u) {
+    const u32x4 x = SEGKV_TOPK_KEYS(u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      atomicAdd(reinterpret_cast<uint32_t*>(hbytes + __builtin_amdgcn_perm(x[e], lane4, 0x0C0C0700u)), 1u);
+  }
+
   uint32_t prefix = 0, eqc = 0;  // eqc: keys equal to the digits fixed so far
   int krem = k;
+  // bin totals: lane q of a quad sums copies 16 q .. 16 q + 15 of bin
+  // 16 wave + lane / 4; the 16-byte pieces are visited in an order rotated by
+  // the bin, so the 16 lanes of a row (4 bins x 4 parts) cover all 64 banks
+  const int my_bin = 16 * wave + (lane >> 2), part = lane & 3;
 #pragma unroll 1
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    const uint32_t fixed = pass == 0 ? 0u : 0xFFFFFFFFu << (shift + 8);  // digits chosen by earlier passes
+    uint32_t* hb = hist + (pass & 1) * kTopkHist;
+    __syncthreads();
+    {
+      const u32x4* hp = reinterpret_cast<const u32x4*>(hb + my_bin * 64 + 16 * part);
+      const u32x4 h0 = hp[my_bin & 3], h1 = hp[(my_bin + 1) & 3], h2 = hp[(my_bin + 2) & 3], h3 = hp[(my_bin + 3) & 3];
+      uint32_t c = ((h0[0] + h0[1]) + (h0[2] + h0[3])) + ((h1[0] + h1[1]) + (h1[2] + h1[3])) +
+                   ((h2[0] + h2[1]) + (h2[2] + h2[3])) + ((h3[0] + h3[1]) + (h3[2] + h3[3]));
+      c += dpp_move<kDppQuadXor1>(c);
+      c += dpp_move<kDppQuadXor2>(c);
+      if (part == 0) reinterpret_cast<uint32_t*>(s_bins)[my_bin] = c;
+    }
+    __syncthreads();
+    {
+      // every wave: lane L holds bins 4 L + i; candidates with digit >= 4 L
+      // by a suffix over the lanes of a 16-lane row, then the rows above
+      const u32x4 t = s_bins[lane];
+      const uint32_t tl = (t[0] + t[1]) + (t[2] + t[3]);
+      uint32_t sfx = tl + dpp_move<kDppRowShl1>(tl);
+      sfx += dpp_move<kDppRowShl2>(sfx);
+      sfx += dpp_move<kDppRowShl4>(sfx);
+      sfx += dpp_move<kDppRowShl8>(sfx);
+      const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 16);
+      const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 32);
+      const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 48);
+      const int row = lane >> 4;
+      sfx += (row < 1 ? r1 : 0u) + (row < 2 ? r2 : 0u) + (row < 3 ? r3 : 0u);
+      // the one (lane, i) with gt < krem <= gt + t[i] holds the k-th largest candidate
+      uint32_t gt = sfx - tl, hit_bin = 0, hit_rem = 0, hit_c = 0;
+      bool hit = false;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        const bool h = gt < (uint32_t)krem && (uint32_t)krem <= gt + t[i];
+        hit_bin = h ? (uint32_t)(4 * lane + i) : hit_bin;
+        hit_rem = h ? (uint32_t)krem - gt : hit_rem;
+        hit_c = h ? t[i] : hit_c;
+        hit = hit || h;
+        gt += t[i];
+      }
+      const int src = (int)__builtin_amdgcn_readfirstlane(__builtin_ctzll(__ballot(hit) | (1ull << 63)));
+      prefix |= (uint32_t)__builtin_amdgcn_readlane((int)hit_bin, src) << shift;
+      krem = __builtin_amdgcn_readlane((int)hit_rem, src);
+      eqc = (uint32_t)__builtin_amdgcn_readlane((int)hit_c, src);
+    }
+    if (eqc == (uint32_t)krem || pass == 3) break;  // every key with these digits is taken, or all digits fixed
+    if (pass < 2) {  // clear this buffer for pass + 2; every wave has summed its bins
+      uint32_t* hz = hb + my_bin * 64 + 16 * part;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) reinterpret_cast<u32x4*>(hz)[c] = u32x4{0, 0, 0, 0};
+    }
+    // count the next digit of the keys that match the digits fixed so far
+    const uint32_t span = 0xFFFFFFFFu >> (8 * (pass + 1));  // x matches iff x - prefix <= span
+    const uint32_t psel = 0x0C000000u | (((pass + 1) & 1) ? 0x00020000u : 0x000C0000u) | ((uint32_t)(6 - pass) << 8);
+    const uint32_t lanebuf = lane4 | 0x00010000u;  // byte 2 = 1 selects the second buffer
 #pragma unroll
     for (int u = 0; u < (S > 0 ? S : ns); ++u) {
       const u32x4 x = SEGKV_TOPK_KEYS(u);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if ((x[e] & fixed) == prefix) atomicAdd(&hist[(((x[e] >> shift) & 255u) << 6) + lane], 1u);
+        if (x[e] - prefix <= span)
+          atomicAdd(reinterpret_cast<uint32_t*>(hbytes + __builtin_amdgcn_perm(x[e], lanebuf, psel)), 1u);
     }
-    __syncthreads();
-    // bin totals: each lane of a quad sums, and clears for the next pass, 16 of
-    // the bin's 64 copies; the 16-byte pieces are visited in an order rotated
-    // by the bin, so the 16 lanes of a row (4 bins x 4 parts) cover all 64 banks
-    const int bin = tid >> 2, part = tid & 3;
-    u32x4* hp = reinterpret_cast<u32x4*>(hist + bin * 64 + 16 * part);
-    const u32x4 h0 = hp[bin & 3], h1 = hp[(bin + 1) & 3], h2 = hp[(bin + 2) & 3], h3 = hp[(bin + 3) & 3];
-    hp[bin & 3] = hp[(bin + 1) & 3] = hp[(bin + 2) & 3] = hp[(bin + 3) & 3] = u32x4{0, 0, 0, 0};
-    uint32_t c = ((h0[0] + h0[1]) + (h0[2] + h0[3])) + ((h1[0] + h1[1]) + (h1[2] + h1[3])) +
-                 ((h2[0] + h2[1]) + (h2[2] + h2[3])) + ((h3[0] + h3[1]) + (h3[2] + h3[3]));
-    c += dpp_move<kDppQuadXor1>(c);
-    c += dpp_move<kDppQuadXor2>(c);
-    // candidates with digit >= bin: suffix over the 4 bins of a 16-lane row,
-    // then the rows above in this wave, then the waves above
-    uint32_t sfx = c + dpp_move<kDppRowShl4>(c);
-    sfx += dpp_move<kDppRowShl8>(sfx);
-    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 16);
-    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 32);
-    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)sfx, 48);
-    const int row = lane >> 4;
-    sfx += (row < 1 ? r1 : 0u) + (row < 2 ? r2 : 0u) + (row < 3 ? r3 : 0u);
-    if (lane == 0) s_wsum[wave] = sfx;  // lane 0 holds the wave's total
-    __syncthreads();
-    uint32_t above = 0;
-#pragma unroll
-    for (int v4 = 0; v4 < kTopkWaves / 4; ++v4) {
-      const u32x4 w4 = reinterpret_cast<const u32x4*>(s_wsum)[v4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) above += 4 * v4 + e > wave ? w4[e] : 0u;
-    }
-    const uint32_t ge = sfx + above, gt = ge - c;
-    if (part == 0 && gt < (uint32_t)krem && (uint32_t)krem <= ge) {
-      s_sel[0] = prefix | ((uint32_t)bin << shift);
-      s_sel[1] = (uint32_t)krem - gt;
-      s_sel[2] = c;
-    }
-    __syncthreads();
-    prefix = s_sel[0];
-    krem = (int)s_sel[1];
-    eqc = s_sel[2];
   }
-
-  // prefix is the k-th largest key. Output order = index order: waves, then
-  // sub-blocks, then lanes, then e. Outputs of up to 16384 indices are staged
-  // in LDS (the histogram space) and copied out coalesced.
-  const bool stage = k <= 256 * 64;
-  uint32_t* s_out = hist;
-  if (eqc == (uint32_t)krem) {
-    // every key >= prefix is taken
-    int g = 0;
+  // prefix is the k-th largest key, or, after an early stop, its leading
+  // digits with zero low bits. Output order = index order: waves, then
+  // sub-blocks, then lanes, then e. Outputs of up to kTopkStageMax indices
+  // are staged in LDS (the histogram space) and copied out coalesced; lanes
+  // that select nothing write to a slot of their own past the staged range.
+  const bool all_eq = eqc == (uint32_t)krem;  // every key >= prefix is taken
+  auto compact = [&](auto staged) __attribute__((always_inline)) {
+    constexpr bool kStage = decltype(staged)::value;
+    const uint32_t dummy = (uint32_t)(kTopkStageMax + lane);
+    auto emit = [&](bool sel, uint32_t pos, int j) __attribute__((always_inline)) {
+      if constexpr (kStage) {
+        hist[sel ? pos : dummy] = (uint32_t)j;
+      } else {
+        if (sel) idx_out[pos] = j;
+      }
+    };
+    if (all_eq) {
+      int g = 0;
 #pragma unroll
-    for (int u = 0; u < (S > 0 ? S : ns); ++u) {
-      const u32x4 x = SEGKV_TOPK_KEYS(u);
+      for (int u = 0; u < (S > 0 ? S : ns); ++u) {
+        const u32x4 x = SEGKV_TOPK_KEYS(u);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) g += __popcll(__ballot(x[e] >= prefix));
+        for (int e = 0; e < 4; ++e) g += __popcll(__ballot(x[e] >= prefix));
+      }
+      if (lane == 0) s_tot[wave][0] = g;
+      __syncthreads();
+      int gb = 0;
+#pragma unroll
+      for (int v = 0; v < kTopkWaves; ++v) gb += v < wave ? s_tot[v][0] : 0;
+#pragma unroll
+      for (int u = 0; u < (S > 0 ? S : ns); ++u) {
+        const u32x4 x = SEGKV_TOPK_KEYS(u);
+        uint64_t m[4];
+        uint32_t pos = (uint32_t)gb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          m[e] = __ballot(x[e] >= prefix);
+          pos = lanes_below(m[e], pos);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool sel = x[e] >= prefix;
+          emit(sel, pos, base + kTopkSub * u + e);
+          pos += sel ? 1u : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gb += __popcll(m[e]);
+      }
+    } else {
+      // keys > prefix, then the first krem keys == prefix
+      int g = 0, q = 0;
+#pragma unroll
+      for (int u = 0; u < (S > 0 ? S : ns); ++u) {
+        const u32x4 x = SEGKV_TOPK_KEYS(u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          g += __popcll(__ballot(x[e] > prefix));
+          q += __popcll(__ballot(x[e] == prefix));
+        }
+      }
+      if (lane == 0) {
+        s_tot[wave][0] = g;
+        s_tot[wave][1] = q;
+      }
+      __syncthreads();
+      int gb = 0, qb = 0;
+#pragma unroll
+      for (int v = 0; v < kTopkWaves; ++v) {
+        gb += v < wave ? s_tot[v][0] : 0;
+        qb += v < wave ? s_tot[v][1] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < (S > 0 ? S : ns); ++u) {
+        const u32x4 x = SEGKV_TOPK_KEYS(u);
+        uint64_t mg[4], mq[4];
+        uint32_t go = (uint32_t)gb, qo = (uint32_t)qb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mg[e] = __ballot(x[e] > prefix);
+          mq[e] = __ballot(x[e] == prefix);
+          go = lanes_below(mg[e], go);
+          qo = lanes_below(mq[e], qo);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool isg = x[e] > prefix, isq = x[e] == prefix;
+          emit(isg || (isq && qo < (uint32_t)krem), go + (qo < (uint32_t)krem ? qo : (uint32_t)krem), base + kTopkSub * u + e);
+          go += isg ? 1u : 0u;
+          qo += isq ? 1u : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gb += __popcll(mg[e]);
+          qb += __popcll(mq[e]);
+        }
+      }
     }
-    if (lane == 0) s_tot[wave][0] = g;
-    __syncthreads();
-    int gb = 0;
-    for (int v = 0; v < wave; ++v) gb += s_tot[v][0];
+    if constexpr (kStage) {
+      __syncthreads();
+      if ((reinterpret_cast<uintptr_t>(idx_out) & 15) == 0) {
+        const int k4 = k >> 2;
+        for (int x = tid; x < k4; x += kTopkThreads)
+          reinterpret_cast<u32x4*>(idx_out)[x] = reinterpret_cast<const u32x4*>(hist)[x];
+        for (int x = 4 * k4 + tid; x < k; x += kTopkThreads) idx_out[x] = (int32_t)hist[x];
+      } else {
+        for (int x = tid; x < k; x += kTopkThreads) idx_out[x] = (int32_t)hist[x];
+      }
+    }
+  };
+  if (S > 0 && S <= kTopkSegSub && all_eq) {
+    // one sweep: wave w stages its selected indices, in order, in its own
+    // segment of 256 S words, then copies them to its place in the output
+    uint32_t* seg = hist + wave * (kTopkSub * SR);
+    uint32_t pos = 0;
 #pragma unroll
-    for (int u = 0; u < (S > 0 ? S : ns); ++u) {
+    for (int u = 0; u < SR; ++u) {
       const u32x4 x = SEGKV_TOPK_KEYS(u);
       uint64_t m[4];
-      int pos = gb;
+      uint32_t p = pos;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         m[e] = __ballot(x[e] >= prefix);
-        pos += lanes_below(m[e]);
+        p = lanes_below(m[e], p);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (x[e] >= prefix) {
-          const int j = base + kTopkSub * u + e;
-          if (stage) s_out[pos] = (uint32_t)j;
-          else idx_out[pos] = j;
-          ++pos;
-        }
+        const bool sel = x[e] >= prefix;
+        if (sel) seg[p] = (uint32_t)(base + kTopkSub * u + e);
+        p += sel ? 1u : 0u;
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) gb += __popcll(m[e]);
+      for (int e = 0; e < 4; ++e) pos += (uint32_t)__popcll(m[e]);
     }
+    if (lane == 0) s_tot[wave][0] = (int)pos;
+    __syncthreads();
+    int off = 0;
+#pragma unroll
+    for (int v = 0; v < kTopkWaves; ++v) off += v < wave ? s_tot[v][0] : 0;
+    int32_t* dst = idx_out + off;
+#pragma unroll 4
+    for (int x = lane; x < (int)pos; x += 64) dst[x] = (int32_t)seg[x];
+  } else if (k <= kTopkStageMax) {
+    compact(std::true_type{});
   } else {
-    // keys > prefix, then the first krem keys == prefix
-    int g = 0, q = 0;
-#pragma unroll
-    for (int u = 0; u < (S > 0 ? S : ns); ++u) {
-      const u32x4 x = SEGKV_TOPK_KEYS(u);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        g += __popcll(__ballot(x[e] > prefix));
-        q += __popcll(__ballot(x[e] == prefix));
-      }
-    }
-    if (lane == 0) {
-      s_tot[wave][0] = g;
-      s_tot[wave][1] = q;
-    }
-    __syncthreads();
-    int gb = 0, qb = 0;
-    for (int v = 0; v < wave; ++v) {
-      gb += s_tot[v][0];
-      qb += s_tot[v][1];
-    }
-#pragma unroll
-    for (int u = 0; u < (S > 0 ? S : ns); ++u) {
-      const u32x4 x = SEGKV_TOPK_KEYS(u);
-      uint64_t mg[4], mq[4];
-      int go = gb, qo = qb;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        mg[e] = __ballot(x[e] > prefix);
-        mq[e] = __ballot(x[e] == prefix);
-        go += lanes_below(mg[e]);
-        qo += lanes_below(mq[e]);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool isg = x[e] > prefix, isq = x[e] == prefix;
-        if (isg || (isq && qo < krem)) {
-          const int pos = go + imin(qo, krem), j = base + kTopkSub * u + e;
-          if (stage) s_out[pos] = (uint32_t)j;
-          else idx_out[pos] = j;
-        }
-        go += isg ? 1 : 0;
-        qo += isq ? 1 : 0;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gb += __popcll(mg[e]);
-        qb += __popcll(mq[e]);
-      }
-    }
-  }
-  if (stage) {
-    __syncthreads();
-    for (int x = tid; x < k; x += kTopkThreads) idx_out[x] = (int32_t)s_out[x];
+    compact(std::false_type{});
   }
 #undef SEGKV_TOPK_KEYS
 }

@@ -84,7 +84,8 @@ def test_mixed_classes_multi_request():
 
 @pytest.mark.parametrize("n,k,levels", [(1000, 100, 7), (33280, 8320, 50), (4096, 4096, 3), (5, 1, 1),
                                         (70000, 1, 0), (2049, 2048, 2), (4097, 100, 0), (61440, 30000, 0),
-                                        (61441, 5, 0), (70000, 35000, 1000), (36864, 36863, 1)])
+                                        (61441, 5, 0), (70000, 35000, 1000), (36864, 36863, 1),
+                                        (70000, 50000, 0), (36864, 30000, 0), (36000, 9000, 0)])
 def test_topk_select_ties(n, k, levels):
     print(f"case topk n={n} k={k} levels={levels}", flush=True)
     x = workloads.uniform_f32(seed=n + k, n=n, levels=levels)
