@@ -227,12 +227,18 @@ __global__ __launch_bounds__(256) void importance_reduce_kernel(const char* __re
   const int off = req_key[r], Lk = req_key[r + 1] - off;
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= Lk) return;
-  uint64_t mk = reinterpret_cast<const uint64_t*>(plan + L.imp_mask_off)[(size_t)r * key_blocks + j / kTileKeys];
+  const uint64_t mk = reinterpret_cast<const uint64_t*>(plan + L.imp_mask_off)[(size_t)r * key_blocks + j / kTileKeys];
+  const float* pj = partial + off + j;
+  // heads in groups of 8: the group's loads are all issued before the adds
   float sum = 0.f;
-  while (mk != 0) {
-    const int h = __builtin_ctzll(mk);
-    mk &= mk - 1;
-    sum += partial[(size_t)h * total_keys + off + j];
+  for (int h0 = 0; h0 < 64 && (mk >> h0) != 0; h0 += 8) {
+    const uint32_t g = (uint32_t)(mk >> h0) & 255u;
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = (g >> i) & 1u ? pj[(size_t)(h0 + i) * total_keys] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((g >> i) & 1u) sum += p[i];
   }
   importance[off + j] = sum;
 }
