@@ -67,11 +67,11 @@ __global__ __launch_bounds__(kImpThreads, 3) void importance_kernel(ImpArgs a) {
   __shared__ int s_pid[kTilePages];  // this head's page at each page of the key block, -1 if none
   __shared__ float colsum[kImpWaves][kTileKeys];
 
-  const ImpItem item = reinterpret_cast<const ImpItem*>(a.plan + a.L.imp_items_off)[blockIdx.x];
+  const ImpItem* itp = reinterpret_cast<const ImpItem*>(a.plan + a.L.imp_items_off) + blockIdx.x;
+  const ImpItem item = *itp;  // indexed below only through itp, so the copy stays in registers
   if (item.pair < 0 || item.pair >= a.R * a.Hkv || item.block < 0) return;  // not a plan of this layout
   const int r = item.pair / a.Hkv, hh = item.pair % a.Hkv;
-  const int sq = a.m.seg_indptr[r + 1] - 1;
-  const int bq = a.m.seg_start[sq], Lq = a.m.seg_len[sq], Lk = bq + Lq;
+  const int bq = item.bq, Lq = item.Lq, Lk = bq + Lq;
   const int kb0 = item.block * kTileKeys;
   if (kb0 >= Lk) return;
   const int n = imin(a.n_last, Lq);
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kImpThreads, 3) void importance_kernel(ImpArgs a) {
   const int U = a.G * nb_head;      // units of this kv head
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lrow = lane & 31, lg = lane >> 5;
-  const int q_base = a.cu_q[r] + Lq - n;  // first of the last n query rows
+  const int q_base = item.cu_q + Lq - n;  // first of the last n query rows
   const int pos_base = Lk - n;            // its position
   const int u_lo = U * wave / kImpWaves, u_hi = U * (wave + 1) / kImpWaves;
 
@@ -95,16 +95,10 @@ __global__ __launch_bounds__(kImpThreads, 3) void importance_kernel(ImpArgs a) {
   };
   if (u_lo < u_hi) q_load(qa, u_lo);
 
-  const HeadView v = head_view_dev(a.m, a.Hkv, r, hh);
   if (tid < kTilePages) {
-    const PageRuns pr = head_page_runs(v);
-    const int page = kb0 / kPage + tid;
-    const int rk = runs_rank(pr, page);
-    int pid = -1;
-    if (runs_rank(pr, page + 1) - rk == 1) {
-      pid = a.page_ids[a.page_indptr[r * a.Hkv + hh] + rk];
-      if (pid < 0 || pid >= a.pool_pages) pid = -1;
-    }
+    const int e = itp->entry[tid];
+    int pid = e >= 0 ? a.page_ids[e] : -1;
+    if (pid < 0 || pid >= a.pool_pages) pid = -1;
     s_pid[tid] = pid;
   }
   // log2-scaled LSE of the last n rows of this head's G query heads, [g][t]
@@ -141,7 +135,7 @@ __global__ __launch_bounds__(kImpThreads, 3) void importance_kernel(ImpArgs a) {
   }
   __syncthreads();
 
-  const int cls = v.cls, W = v.W;
+  const int cls = item.cls, W = item.W;
   const bool pages_full = s_pid[0] >= 0 && s_pid[1] >= 0 && s_pid[2] >= 0 && s_pid[3] >= 0;
   const int pa = s_pid[lrow >> 4], pb = s_pid[2 + (lrow >> 4)];
   const int j0 = pa < 0 ? INT_MAX : kb0 + lrow;
@@ -205,7 +199,7 @@ __global__ __launch_bounds__(kImpThreads, 3) void importance_kernel(ImpArgs a) {
   }
   __syncthreads();
   if (tid < kTileKeys && kb0 + tid < Lk) {
-    const int off = reinterpret_cast<const int32_t*>(a.plan + a.L.req_key_off)[r];  // request r's first key
+    const int off = item.key_off;  // request r's first key
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < kImpWaves; ++w) sum += colsum[w][tid];

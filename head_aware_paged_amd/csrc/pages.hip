@@ -123,9 +123,10 @@ __device__ PairInfo pair_info(const PagesArgs& a, int k) {
   return p;
 }
 
-// One launch: block 0 plans, every other block fills up to 1024 table entries
-// of one (request, kv head) pair. A fill block derives its pair's CSR offsets
-// itself, so it does not wait for the planning block.
+// One launch: block 0 plans; fill blocks each fill up to 1024 table entries of
+// one (request, kv head) pair; mask blocks write the importance head masks;
+// item blocks write up to 1024 importance items each. Fill and item blocks
+// derive the offsets they need themselves, so no block waits for another.
 __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fill_blocks_per_pair) {
   __shared__ int s[kScanThreads];
   __shared__ int sseg[kScanThreads];  // fill blocks: segment starts of the pair's request
@@ -140,6 +141,54 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
   const int n_pairs = a.R * a.Hkv;
 
   const int n_fill = n_pairs * fill_blocks_per_pair;
+  const int n_mask = a.R * cdiv(a.key_blocks, kScanThreads);
+  if ((int)blockIdx.x > n_fill + n_mask) {
+    // ---------------- importance items [c * 1024, (c + 1) * 1024) ----------------
+    // every 64-key block of every table, pair by pair; this block derives the
+    // pairs' table offsets, item offsets and the requests' key offsets itself
+    const int c = blockIdx.x - 1 - n_fill - n_mask;
+    for (int k = tid; k < n_pairs; k += kScanThreads) info[k] = pair_info(a, k);
+    __syncthreads();
+    int it_tot[3];
+    block_scan<3>(
+        n_pairs,
+        [&](int k, int (&v)[3]) {
+          v[0] = runs_count(info[k].pr);
+          v[1] = runs_count(block_runs(info[k].pr));
+          v[2] = k % a.Hkv == 0 ? info[k].bq + info[k].Lq : 0;
+        },
+        [&](int k, const int (&p)[3]) {
+          info[k].tbase = p[0];
+          pair_imp[k] = p[1];
+          if (k % a.Hkv == 0) req_off[k / a.Hkv] = p[2];
+        },
+        it_tot, s);
+    ImpItem* imp_items = reinterpret_cast<ImpItem*>(a.plan + a.L.imp_items_off);
+    const int x = c * kScanThreads + tid;
+    if (x >= imin(it_tot[1], a.n_imp_items)) return;
+    int lo = 0, hi = n_pairs - 1;  // pair: last k with pair_imp[k] <= x
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pair_imp[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    const PairInfo& pi = info[lo];
+    ImpItem it;
+    it.pair = lo;
+    it.block = runs_page(block_runs(pi.pr), x - pair_imp[lo]);
+    it.cls = pi.cls;
+    it.W = pi.W;
+    it.bq = pi.bq;
+    it.Lq = pi.Lq;
+    it.cu_q = pi.cu_q;
+    it.key_off = req_off[lo / a.Hkv];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int page = it.block * (kTileKeys / kPage) + i, rk = runs_rank(pi.pr, page);
+      it.entry[i] = runs_rank(pi.pr, page + 1) - rk == 1 ? pi.tbase + rk : -1;
+    }
+    imp_items[x] = it;
+    return;
+  }
   if ((int)blockIdx.x > n_fill) {
     // ---------------- importance head masks of request r, blocks [c * 1024, ...) ----------------
     // (kv heads <= 64; otherwise no masks are written)
@@ -371,17 +420,7 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
       [&](int r, const int (&p)[1]) { req_key[r] = p[0]; }, kt, s);
   if (tid == 0) req_key[a.R] = kt[0];
 
-  // importance items: every 64-key block of every table, pair by pair
-  const int n_imp = pt[2];
-  ImpItem* imp_items = reinterpret_cast<ImpItem*>(a.plan + a.L.imp_items_off);
-  for (int x = tid; x < imin(n_imp, a.n_imp_items); x += kScanThreads) {
-    int lo = 0, hi = n_pairs - 1;  // pair: last k with pair_imp[k] <= x
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pair_imp[mid] <= x) lo = mid; else hi = mid - 1;
-    }
-    imp_items[x] = ImpItem{lo, runs_page(block_runs(info[lo].pr), x - pair_imp[lo])};
-  }
+  const int n_imp = pt[2];  // importance items (written by the item blocks)
   if (tid == 0) {
     PlanHeader h;
     h.n_mtiles = n_mt;
@@ -519,7 +558,8 @@ extern "C" int32_t segkv_build_pages(const segkv_dims* dims, const segkv_meta* m
   }
   const int per_pair = cdiv(max_pages, kScanThreads);
   const int mask_blocks = a.R * cdiv(hp.key_blocks, kScanThreads);
-  build_kernel<<<1 + a.R * a.Hkv * per_pair + mask_blocks, kScanThreads, 0, s>>>(a, per_pair);
+  const int item_blocks = cdiv(hp.n_imp_items, kScanThreads);
+  build_kernel<<<1 + a.R * a.Hkv * per_pair + mask_blocks + item_blocks, kScanThreads, 0, s>>>(a, per_pair);
   SEGKV_LAUNCH_CHECK();
   return SEGKV_OK;
 }

@@ -220,9 +220,14 @@ struct Item {
 constexpr int kXcds = 8;
 SEGKV_HD int xcd_slot(int p, int q8) { return kXcds * (p % q8) + p / q8; }
 
-// Importance work item: one 64-key block of one (request, kv head) table.
+// Importance work item: one 64-key block of one (request, kv head) table,
+// with what its work-group needs before it reads the block's page ids.
 struct ImpItem {
   int32_t pair, block;
+  int32_t cls, W;          // the kv head's class and window
+  int32_t bq, Lq;          // the request's query segment: start position and length
+  int32_t cu_q, key_off;   // the request's first Q row and first key of the importance vector
+  int32_t entry[4];        // table entry of each of the block's 4 pages, -1 when the table has none
 };
 
 struct PlanLayout {
