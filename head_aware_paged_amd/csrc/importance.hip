@@ -84,8 +84,36 @@ __global__ __launch_bounds__(kImpThreads, 3) void importance_kernel(ImpArgs a) {
   const int pos_base = Lk - n;            // its position
   const int u_lo = U * wave / kImpWaves, u_hi = U * (wave + 1) / kImpWaves;
 
-  // the wave's first Q fragment (A operand: Q row tb + lrow of query head hg)
-  // is requested before the page lookups, so its latency overlaps them
+  // Every load of the prologue is issued before any is waited for: the
+  // block's page ids (scalar loads), the LSE of its rows, the K tile, and the
+  // wave's first Q fragment (A operand: Q row tb + lrow of query head hg).
+  // Addresses are clamped into range and unused values dropped afterwards,
+  // so no load sits behind a branch.
+  int ent[kTilePages], pid[kTilePages];
+#pragma unroll
+  for (int u = 0; u < kTilePages; ++u) ent[u] = itp->entry[u];
+#pragma unroll
+  for (int u = 0; u < kTilePages; ++u) pid[u] = a.page_ids[imax(ent[u], 0)];
+  const int pool_pages = a.pool_pages < INT32_MAX ? (int)a.pool_pages : INT32_MAX;
+#pragma unroll
+  for (int u = 0; u < kTilePages; ++u) pid[u] = ent[u] < 0 || pid[u] < 0 || pid[u] >= pool_pages ? -1 : pid[u];
+  // log2-scaled LSE of the last n rows of this head's G query heads, [g][t]
+  // with t < NP (rows past n repeat row n - 1)
+  const int n_lse = a.G * NP;
+  auto lse_at = [&](int x) { return a.lse[(size_t)(q_base + imin(x % NP, n - 1)) * a.Hq + hh * a.G + x / NP]; };
+  float lv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) lv[u] = lse_at(imin(tid + u * kImpThreads, n_lse - 1));
+  // K tile rows: qd = tid + u * kImpThreads is 16-byte chunk qd % KCH of key
+  // qd / KCH; rows of missing pages are zero
+  u32x4 kr[KLOADS];
+#pragma unroll
+  for (int u = 0; u < KLOADS; ++u) {
+    const int qd = tid + u * kImpThreads, key = qd / KCH, c = qd % KCH;
+    const int pg = pid[key >> 4];
+    kr[u] = *reinterpret_cast<const u32x4*>(a.k_pool + ((size_t)imax(pg, 0) * kPage + (key & 15)) * D + 8 * c);
+    if (pg < 0) kr[u] = u32x4{0, 0, 0, 0};
+  }
   bf16x8 qa[KS];
   auto q_load = [&](bf16x8* dst, int uu) {
     const int hg = uu / nb_head, tb = (uu % nb_head) * 32;
@@ -95,43 +123,20 @@ __global__ __launch_bounds__(kImpThreads, 3) void importance_kernel(ImpArgs a) {
   };
   if (u_lo < u_hi) q_load(qa, u_lo);
 
-  if (tid < kTilePages) {
-    const int e = itp->entry[tid];
-    int pid = e >= 0 ? a.page_ids[e] : -1;
-    if (pid < 0 || pid >= a.pool_pages) pid = -1;
-    s_pid[tid] = pid;
+  if (tid == 0) {
+#pragma unroll
+    for (int u = 0; u < kTilePages; ++u) s_pid[u] = pid[u];
   }
-  // log2-scaled LSE of the last n rows of this head's G query heads, [g][t]
-  // with t < NP (rows past n repeat row n - 1); loads first, then stores
-  for (int x0 = 0; x0 < a.G * NP; x0 += 4 * kImpThreads) {
-    float lv[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int x = x0 + u * kImpThreads + tid;
-      lv[u] = x < a.G * NP ? a.lse[(size_t)(q_base + imin(x % NP, n - 1)) * a.Hq + hh * a.G + x / NP] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int x = x0 + u * kImpThreads + tid;
-      if (x < a.G * NP) s_lse[x] = lv[u] * kLog2e;
-    }
+  for (int u = 0; u < 4; ++u) {
+    const int x = tid + u * kImpThreads;
+    if (x < n_lse) s_lse[x] = lv[u] * kLog2e;
   }
-  __syncthreads();
-  // K tile -> LDS (rows of missing pages are zero)
-  {
-    u32x4 kr[KLOADS];
+  for (int x = tid + 4 * kImpThreads; x < n_lse; x += kImpThreads) s_lse[x] = lse_at(x) * kLog2e;
 #pragma unroll
-    for (int u = 0; u < KLOADS; ++u) {
-      const int qd = tid + u * kImpThreads, key = qd / KCH, c = qd % KCH;
-      const int pid = s_pid[key >> 4];
-      kr[u] = pid >= 0 ? *reinterpret_cast<const u32x4*>(a.k_pool + ((size_t)pid * kPage + (key & 15)) * D + 8 * c)
-                       : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < KLOADS; ++u) {
-      const int qd = tid + u * kImpThreads;
-      *reinterpret_cast<u32x4*>(&ks[(qd / KCH) * kStride + 8 * (qd % KCH)]) = kr[u];
-    }
+  for (int u = 0; u < KLOADS; ++u) {
+    const int qd = tid + u * kImpThreads;
+    *reinterpret_cast<u32x4*>(&ks[(qd / KCH) * kStride + 8 * (qd % KCH)]) = kr[u];
   }
   __syncthreads();
 
