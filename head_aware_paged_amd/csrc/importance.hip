@@ -52,18 +52,21 @@ constexpr int kImpMaxLse = 4096;  // Hq * (n_last rounded up to 32) values (boun
 // wave w taking units [U w / 4, U (w + 1) / 4), and writes the block's 64
 // partial sums; a second kernel adds, key by key, the partials of the heads
 // whose tables touch the key's block, in head order. Each score is thus summed
-// in a fixed order with no float atomics. K and Q fragments go from memory
-// straight into MFMA operand registers; the next unit's Q is in flight while
-// the current one computes; units whose 32 rows see all 64 keys skip every
-// mask.
+// in a fixed order with no float atomics. The K tile is staged in LDS. A
+// unit's Q block is fetched whole rows per load instruction (a quarter of the
+// cache-line requests that MFMA-order loads would make) and passes through the
+// wave's own LDS slot; the next unit's Q is in flight while the current one
+// computes. Units whose 32 rows see all 64 keys skip every mask.
 template <int D>
 __global__ __launch_bounds__(kImpThreads, 3) void importance_kernel(ImpArgs a) {
   constexpr int KS = D / 16;
   constexpr int KCH = D / 8;            // 16-byte chunks per key row
   constexpr int kStride = D + 8;        // padded LDS row (elements)
   constexpr int KLOADS = kTileKeys * KCH / kImpThreads;
+  constexpr int CH = D / 8;              // 16-byte chunks per Q row
   __shared__ __attribute__((aligned(16))) uint16_t ks[kTileKeys * kStride];
-  __shared__ __attribute__((aligned(16))) float s_lse[kImpMaxLse];
+  __shared__ __attribute__((aligned(16))) uint16_t qs[kImpWaves][32 * D];  // each wave's unit Q, chunks swizzled
+  extern __shared__ __attribute__((aligned(16))) float s_lse[];  // G * NP values (size set at launch)
   __shared__ int s_pid[kTilePages];  // this head's page at each page of the key block, -1 if none
   __shared__ float colsum[kImpWaves][kTileKeys];
 
@@ -114,14 +117,29 @@ __global__ __launch_bounds__(kImpThreads, 3) void importance_kernel(ImpArgs a) {
     kr[u] = *reinterpret_cast<const u32x4*>(a.k_pool + ((size_t)imax(pg, 0) * kPage + (key & 15)) * D + 8 * c);
     if (pg < 0) kr[u] = u32x4{0, 0, 0, 0};
   }
-  bf16x8 qa[KS];
-  auto q_load = [&](bf16x8* dst, int uu) {
+  // A unit's 32 x D block of Q is fetched with 16-byte chunk lane + 64 i per
+  // lane (whole rows per instruction), passes through the wave's LDS slot with
+  // chunk c of row r at c ^ (r mod CH), and is read back in MFMA A-operand
+  // order (row lrow, dims 16 k8 + 8 lg .. + 8).
+  u32x4 qr[KS];
+  auto q_fetch = [&](int uu) __attribute__((always_inline)) {
     const int hg = uu / nb_head, tb = (uu % nb_head) * 32;
-    const uint16_t* qp = a.q + ((size_t)(q_base + imin(tb + lrow, n - 1)) * a.Hq + hh * a.G + hg) * D + 8 * lg;
 #pragma unroll
-    for (int k8 = 0; k8 < KS; ++k8) dst[k8] = *reinterpret_cast<const bf16x8*>(qp + 16 * k8);
+    for (int i = 0; i < KS; ++i) {
+      const int qc = lane + 64 * i, row = qc / CH, c = qc % CH;
+      qr[i] = *reinterpret_cast<const u32x4*>(
+          a.q + ((size_t)(q_base + imin(tb + row, n - 1)) * a.Hq + hh * a.G + hg) * D + 8 * c);
+    }
   };
-  if (u_lo < u_hi) q_load(qa, u_lo);
+  uint16_t* const qw = qs[wave];
+  auto q_commit = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const int qc = lane + 64 * i, row = qc / CH, c = qc % CH;
+      *reinterpret_cast<u32x4*>(qw + row * D + 8 * (c ^ (row & (CH - 1)))) = qr[i];
+    }
+  };
+  if (u_lo < u_hi) q_fetch(u_lo);
 
   if (tid == 0) {
 #pragma unroll
@@ -147,20 +165,31 @@ __global__ __launch_bounds__(kImpThreads, 3) void importance_kernel(ImpArgs a) {
   const int j1 = pb < 0 ? INT_MAX : kb0 + 32 + lrow;
 
   float acc0 = 0.f, acc1 = 0.f;  // keys lrow and 32 + lrow, this lane's rows
-  // unit uu with Q in qa; once its MFMAs have read qa, the next unit's Q is
-  // requested into qa, so that load overlaps this unit's exponentials
+  // unit uu: its Q goes from the fetch registers to the wave's LDS slot; once
+  // the MFMAs have read it, the next unit's fetch is issued, so that load
+  // overlaps this unit's exponentials
   auto unit = [&](int uu) {
+    q_commit();
     f32x16 s0, s1;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
 #pragma unroll
     for (int k8 = 0; k8 < KS; ++k8) {  // B operand: key 32 kb + lrow, dims 16 k8 + 8 lg .. + 8
+      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qw + lrow * D + 8 * ((2 * k8 + lg) ^ (lrow & (CH - 1))));
       const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(&ks[lrow * kStride + 16 * k8 + 8 * lg]);
       const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(&ks[(32 + lrow) * kStride + 16 * k8 + 8 * lg]);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[k8], k0, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[k8], k1, s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qv, k0, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qv, k1, s1, 0, 0, 0);
     }
-    if (uu + 1 < u_hi) q_load(qa, uu + 1);
+    // operand reads two k-steps ahead of their MFMAs (bounds the live fragments)
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int k8 = 0; k8 < KS - 2; ++k8) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    if (uu + 1 < u_hi) q_fetch(uu + 1);
     // lane holds keys (j0, j1) for rows t = tb + 8(i/4) + 4 lg + i%4 of query head hg
     const int hg = uu / nb_head, tb = (uu % nb_head) * 32;
     const float* lse_h = &s_lse[hg * NP + tb + 4 * lg];
@@ -663,10 +692,11 @@ extern "C" int32_t token_importance_topk(const segkv_dims* dims, const segkv_met
   a.n_last = n_last;
   if (R > 65535) return fail(SEGKV_ERR_UNSUPPORTED, "importance supports at most 65535 requests");
   if (hp.n_imp_items > 0) {
+    const size_t lse_bytes = sizeof(float) * (size_t)G * 32 * (size_t)cdiv(n_last, 32);  // G * NP of any request
     if (dims->head_dim == 128)
-      importance_kernel<128><<<hp.n_imp_items, kImpThreads, 0, s>>>(a);
+      importance_kernel<128><<<hp.n_imp_items, kImpThreads, lse_bytes, s>>>(a);
     else
-      importance_kernel<64><<<hp.n_imp_items, kImpThreads, 0, s>>>(a);
+      importance_kernel<64><<<hp.n_imp_items, kImpThreads, lse_bytes, s>>>(a);
     SEGKV_LAUNCH_CHECK();
   }
   importance_reduce_kernel<<<dim3(cdiv(max_lk, 256), R), 256, 0, s>>>(a.plan, a.L, a.partial, importance_dev,
