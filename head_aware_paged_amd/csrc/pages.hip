@@ -36,11 +36,32 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 // N exclusive prefix sums at once over n items: value(i, v) fills v[0..N),
 // write(i, p) receives the prefixes; totals[] receives the sums (uniform
 // across the block). Block-wide, all threads call it; s holds at least
-// N * kScanThreads / 64 ints. Two barriers per 1024 items.
+// N * kScanThreads / 64 ints. Two barriers per 1024 items; up to 64 items take one wave.
 template <int N, class F, class W>
 __device__ void block_scan(int n, F value, W write, int (&totals)[N], int* s) {
   constexpr int NW = kScanThreads / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (n <= 64) {
+    // one wave scans, the others only wait for the totals: one barrier
+    if (wave == 0) {
+      int v[N], p[N];
+#pragma unroll
+      for (int c = 0; c < N; ++c) v[c] = 0;
+      if (lane < n) value(lane, v);
+#pragma unroll
+      for (int c = 0; c < N; ++c) {
+        const int x = wave_inclusive_scan(v[c]);
+        p[c] = x - v[c];
+        if (lane == 63) s[c] = x;
+      }
+      if (lane < n) write(lane, p);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < N; ++c) totals[c] = s[c];
+    __syncthreads();  // s is free again for the next scan
+    return;
+  }
   int carry[N];
 #pragma unroll
   for (int c = 0; c < N; ++c) carry[c] = 0;
