@@ -503,36 +503,44 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
   }
 
   const float l_row = l_run + __shfl_xor(l_run, 32);
-  if (mt.partial_base < 0) {
-    if (!row_valid) return;
-    const float inv = 1.f / l_row;
-    uint16_t* op = a.out + ((size_t)qrow * a.Hq + qhead) * D;
+  // O leaves through LDS: the lane's O^T fragment (its row, 4-wide d groups)
+  // goes to a per-wave [32 rows][D] block, 16-byte chunks XOR-swizzled by
+  // row, and comes back whole rows per instruction, so every store writes
+  // full rows (writing the fragments directly puts 32 rows in every store)
+  const bool split = mt.partial_base >= 0;
+  const float inv = l_row > 0.f ? 1.f / l_row : 0.f;  // a chunk may hold no key of a row: O_c = 0, l_c = 0
+  __syncthreads();  // every wave's last PV product has read its V stage
+  constexpr int OCH = D / 8;  // 16-byte chunks per row
+  uint16_t* ostage = ((wave >> 1) == 0 ? sk0 : (wave >> 1) == 1 ? sk1 : (wave >> 1) == 2 ? sk2 : sv0) +
+                     (wave & 1) * 32 * D;
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+  for (int b = 0; b < DB; ++b)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * b + 8 * g4 + 4 * lg;
-        *reinterpret_cast<bf16x4*>(op + d) =
-            bf16x4{(__bf16)(o_acc[b][4 * g4 + 0] * inv), (__bf16)(o_acc[b][4 * g4 + 1] * inv),
-                   (__bf16)(o_acc[b][4 * g4 + 2] * inv), (__bf16)(o_acc[b][4 * g4 + 3] * inv)};
-      }
-    if (a.lse != nullptr && lg == 0) a.lse[(size_t)qrow * a.Hq + qhead] = (m_run + log2f(l_row)) * kLn2;
-  } else {
-    char* slot = a.partials + (size_t)(mt.partial_base + it.chunk) * partial_slot_bytes(D);
-    uint16_t* po = reinterpret_cast<uint16_t*>(slot) + (size_t)rm * D;
-    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;  // a row may see no key of this chunk: O_c = 0, l_c = 0
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int c = 4 * b + g4;  // d = 32 b + 8 g4 + 4 lg .. + 4
+      *reinterpret_cast<bf16x4*>(ostage + lrow * D + 8 * (c ^ (lrow & (OCH - 1))) + 4 * lg) =
+          bf16x4{(__bf16)(o_acc[b][4 * g4 + 0] * inv), (__bf16)(o_acc[b][4 * g4 + 1] * inv),
+                 (__bf16)(o_acc[b][4 * g4 + 2] * inv), (__bf16)(o_acc[b][4 * g4 + 3] * inv)};
+    }
+  char* slot = split ? a.partials + (size_t)(mt.partial_base + it.chunk) * partial_slot_bytes(D) : nullptr;
+  constexpr int RPI = 64 / OCH;  // rows per read-back instruction
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * b + 8 * g4 + 4 * lg;
-        *reinterpret_cast<bf16x4*>(po + d) =
-            bf16x4{(__bf16)(o_acc[b][4 * g4 + 0] * inv), (__bf16)(o_acc[b][4 * g4 + 1] * inv),
-                   (__bf16)(o_acc[b][4 * g4 + 2] * inv), (__bf16)(o_acc[b][4 * g4 + 3] * inv)};
-      }
-    if (lg == 0) {
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = RPI * i + lane / OCH, c = lane % OCH;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ostage + r * D + 8 * (c ^ (r & (OCH - 1))));
+    const int rmr = wave * 32 + r, hgr = rmr / MP, pr = rmr % MP;
+    if (split) {
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(slot) + (size_t)rmr * D + 8 * c) = v;
+    } else if (pr < mt.n_pos) {
+      *reinterpret_cast<u32x4*>(a.out + ((size_t)(mt.q_row0 + pr) * a.Hq + mt.h * a.G + hgr) * D + 8 * c) = v;
+    }
+  }
+  if (lg == 0) {
+    if (split) {
       float* ml = reinterpret_cast<float*>(slot + partial_o_bytes(D)) + 2 * rm;
       *reinterpret_cast<f32x2*>(ml) = f32x2{m_run, l_row};
+    } else if (row_valid && a.lse != nullptr) {
+      a.lse[(size_t)qrow * a.Hq + qhead] = (m_run + log2f(l_row)) * kLn2;
     }
   }
 }
