@@ -35,6 +35,14 @@ def small_variants():
     yield workloads.make_custom("mha_g1", Hq=3, Hkv=3, D=64, theta=1e4,
                                 seg_lens_per_req=[[160, 200]], orig_starts_per_req=[[0, None]],
                                 classes=[G_, L_, D_], windows=[0, 64, 0])
+    # 18 requests x 4 kv heads: more than 64 (request, kv head) pairs and m-tiles,
+    # so the planning sums take their multi-wave path
+    nreq = 18
+    yield workloads.make_custom("many_req", Hq=8, Hkv=4, D=64, theta=1e4,
+                                seg_lens_per_req=[[48 + 16 * (r % 4), 30 + 11 * (r % 5)] for r in range(nreq)],
+                                orig_starts_per_req=[[3 * r, None] for r in range(nreq)],
+                                classes=[(G_, L_, D_, L_)[(r + h) % 4] for r in range(nreq) for h in range(4)],
+                                windows=[(0, 24, 0, 9)[(r + h) % 4] for r in range(nreq) for h in range(4)])
 
 
 SMALL_NAMES = [w.name for w in small_variants()]

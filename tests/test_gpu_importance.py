@@ -82,6 +82,21 @@ def test_mixed_classes_multi_request():
     check(w, imp, idx, 20, k)
 
 
+def test_many_requests():
+    """18 requests x 4 kv heads: more than 64 pairs, so the build kernel's
+    importance item blocks take their multi-wave sums."""
+    nreq = 18
+    w = workloads.make_custom("many_req", Hq=8, Hkv=4, D=64, theta=1e4,
+                              seg_lens_per_req=[[48 + 16 * (r % 4), 30 + 11 * (r % 5)] for r in range(nreq)],
+                              orig_starts_per_req=[[3 * r, None] for r in range(nreq)],
+                              classes=[(G_, L_, D_, L_)[(r + h) % 4] for r in range(nreq) for h in range(4)],
+                              windows=[(0, 24, 0, 9)[(r + h) % 4] for r in range(nreq) for h in range(4)])
+    print("case many_req: importance + top-k, 18 requests, n_last 16", flush=True)
+    k = [(r * 7) % 40 for r in range(nreq)]
+    imp, idx = run(w, 16, k)
+    check(w, imp, idx, 16, k)
+
+
 @pytest.mark.parametrize("n,k,levels", [(1000, 100, 7), (33280, 8320, 50), (4096, 4096, 3), (5, 1, 1),
                                         (70000, 1, 0), (2049, 2048, 2), (4097, 100, 0), (61440, 30000, 0),
                                         (61441, 5, 0), (70000, 35000, 1000), (36864, 36863, 1),
