@@ -15,7 +15,9 @@ function's docstring.
 Parity status per function:
   bf16 rounding, rope/relocate, visibility (two independent routines),
   page tables, spans, move lists, attention (brute force + vectorised),
-  importance, top-k, sparse FFN: pinned by ``tests/test_oracle_*.py``.
+  decode attention (brute force + vectorised, and against the prefill
+  attention of a one-token-longer query segment), importance, top-k, sparse
+  FFN: pinned by ``tests/test_oracle_*.py``.
   Agreement with RedKnot's own implementation (its RoPE pairing, window
   inclusivity, dense-vs-global semantics) cannot be pinned: the pages print
   no worked example. That end-to-end numerical match is "parity unpinned".
@@ -26,5 +28,6 @@ from .store import gather_kv, gather_cache_k  # noqa: F401
 from .visibility import (visible_brute, visible_intervals, page_table, page_tables,  # noqa: F401
                          visible_spans, move_list, visible_count, row_position)
 from .attention import attention, attention_brute  # noqa: F401
+from .decode import decode, decode_brute  # noqa: F401
 from .importance import importance, topk_select  # noqa: F401
 from .ffn import sparse_ffn  # noqa: F401

@@ -53,6 +53,16 @@ def _normal_bf16(rng: np.random.Generator, shape, std: float = 1.0, draw: bool =
     return out.reshape(shape)
 
 
+def decode_inputs(w, seed: int = 0):
+    """Inputs of one decode step: the new token of every request, at position
+    L_k(r). Returns (q_new [R, Hq, D], k_new [R, Hkv, D], v_new [R, Hkv, D]),
+    bf16 bit patterns drawn like the workload's own Q and K/V (standard
+    normal). Input recipe only."""
+    rng = np.random.Generator(np.random.PCG64(10_000 + seed))
+    R, Hq, Hkv, D = w.num_requests, w.num_q_heads, w.num_kv_heads, w.head_dim
+    return (_normal_bf16(rng, (R, Hq, D)), _normal_bf16(rng, (R, Hkv, D)), _normal_bf16(rng, (R, Hkv, D)))
+
+
 @dataclasses.dataclass
 class Workload:
     """One synthetic batch. Arrays holding bf16 data are uint16 bit patterns.
