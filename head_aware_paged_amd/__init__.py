@@ -23,6 +23,7 @@ GLOBAL, LOCAL, RETRIEVAL, DENSE = 0, 1, 2, 3
 EXPORTS = [
     "segkv_status_string", "segkv_last_error", "segkv_plan_sizes", "segkv_build_pages",
     "segkv_visible_spans", "rope_relocate", "segpaged_attn_prefill", "token_importance_topk",
+    "segkv_decode_workspace_size", "segpaged_attn_decode",
     "segkv_topk_select", "sparse_ffn_workspace_size", "sparse_ffn_swiglu",
 ]
 
@@ -74,6 +75,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "segkv_visible_spans": ([P, P, P, P, P, P], I32),
         "rope_relocate": ([P, P, P, P, I64, I64, P, P, P, I32, I32, I32, F64, P], I32),
         "segpaged_attn_prefill": ([P, P, P, P, P, I64, P, P, P, SZ, F32, P, P, P, SZ, P], I32),
+        "segkv_decode_workspace_size": ([P, P, P], I32),
+        "segpaged_attn_decode": ([P, P, P, P, P, P, P, P, I64, P, P, P, F32, P, P, P, SZ, P], I32),
         "token_importance_topk": ([P, P, P, P, P, P, I64, P, P, P, P, SZ, P, F32, I32, P, P, P, P, SZ, P], I32),
         "segkv_topk_select": ([P, I32, I32, P, P], I32),
         "sparse_ffn_workspace_size": ([I32, I32], SZ),
@@ -189,6 +192,27 @@ def segpaged_attn_prefill(d: Dims, meta: HostMeta, q, k_pool, v_pool, page_ids, 
         ctypes.byref(d), ctypes.byref(ms), _ptr(q), _ptr(k_pool), _ptr(v_pool), k_pool.shape[0], _ptr(page_ids),
         _ptr(page_pos), _ptr(plan), plan.numel() * plan.element_size(), float(softmax_scale), _ptr(out),
         _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def segkv_decode_workspace_size(d: Dims, meta: HostMeta) -> int:
+    lib = load()
+    ms = meta.struct()
+    n = ctypes.c_size_t(0)
+    _check("segkv_decode_workspace_size", lib.segkv_decode_workspace_size(ctypes.byref(d), ctypes.byref(ms),
+                                                                          ctypes.byref(n)))
+    return int(n.value)
+
+
+def segpaged_attn_decode(d: Dims, meta: HostMeta, dmeta: DeviceMeta, q_new, k_new, v_new, k_pool, v_pool,
+                         page_indptr, page_ids, page_pos, softmax_scale: float, out, lse=None, workspace=None,
+                         stream=None):
+    lib = load()
+    ms, dm = meta.struct(), dmeta.struct()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("segpaged_attn_decode", lib.segpaged_attn_decode(
+        ctypes.byref(d), ctypes.byref(ms), ctypes.byref(dm), _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
+        _ptr(v_pool), k_pool.shape[0], _ptr(page_indptr), _ptr(page_ids), _ptr(page_pos), float(softmax_scale),
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def token_importance_topk(d: Dims, meta: HostMeta, dmeta: DeviceMeta, cu_q, q, k_pool, page_indptr, page_ids,

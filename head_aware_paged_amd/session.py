@@ -17,8 +17,9 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (HostMeta, dims, rope_relocate, segkv_build_pages, segkv_plan_sizes, segkv_visible_spans,
-               segpaged_attn_prefill, sparse_ffn_swiglu, sparse_ffn_workspace_size, token_importance_topk)
+from . import (HostMeta, dims, rope_relocate, segkv_build_pages, segkv_decode_workspace_size, segkv_plan_sizes,
+               segkv_visible_spans, segpaged_attn_decode, segpaged_attn_prefill, sparse_ffn_swiglu,
+               sparse_ffn_workspace_size, token_importance_topk)
 
 
 class SegPagedLayer:
@@ -82,6 +83,22 @@ class SegPagedLayer:
             lse = torch.empty(T, Hq, dtype=torch.float32, device=self.device)
         segpaged_attn_prefill(self.dims, self.meta, q, k_pool, v_pool, self.page_ids, self.page_pos, self.plan,
                               self.scale, out, lse, self.workspace, stream=stream)
+        return out, lse
+
+    def decode(self, q_new, k_new, v_new, k_pool, v_pool, out=None, lse=None, want_lse=True, stream=None):
+        """One new query row per request at position L_k(r) over the same page tables.
+        q_new: [R][Hq][D]; k_new, v_new: [R][Hkv][D] bf16."""
+        R, Hq, D = self.dims.num_requests, self.dims.num_q_heads, self.dims.head_dim
+        if out is None:
+            out = torch.empty(R, Hq, D, dtype=torch.bfloat16, device=self.device)
+        if lse is None and want_lse:
+            lse = torch.empty(R, Hq, dtype=torch.float32, device=self.device)
+        if not hasattr(self, "dec_workspace"):
+            nbytes = segkv_decode_workspace_size(self.dims, self.meta)
+            self.dec_workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.device)
+        segpaged_attn_decode(self.dims, self.meta, self.dmeta, q_new, k_new, v_new, k_pool, v_pool,
+                             self.page_indptr, self.page_ids, self.page_pos, self.scale, out, lse,
+                             self.dec_workspace, stream=stream)
         return out, lse
 
     def importance_topk(self, q, k_pool, lse, n_last: int, k: Optional[Sequence[int]], importance=None,

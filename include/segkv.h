@@ -187,6 +187,31 @@ int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_meta* meta_hos
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode-phase attention: one new query row per request, the next step of the
+ * same requests (arXiv abstract: long-context generation; paooo.com
+ * "如何使用RedKnot": EXECUTE over the visible state chosen per head).
+ * The new token of request r sits at position i = L_k(r), right after its
+ * query segment. Query head g (kv head h = g / G) attends over the keys the
+ * class rule of the prefill gives position i: GLOBAL and DENSE every key,
+ * LOCAL(W) the query segment and positions i-W+1..i, RETRIEVAL the query
+ * segment and the two reused segments; always including the new token itself.
+ * Stored keys are read through the page tables that segkv_build_pages wrote
+ * for this layout (page_indptr/page_ids/page_pos, unchanged).
+ * q_new: [R][Hq][D] bf16 (RoPE at i); k_new, v_new: [R][Hkv][D] bf16, the new
+ * token's key (RoPE at i) and value. Pools as in segpaged_attn_prefill.
+ * out: [R][Hq][D] bf16; lse: [R][Hq] fp32 natural log (nullable).
+ * workspace: segkv_decode_workspace_size bytes (may be NULL when that is 0).
+ * Limits: D in {64, 128}, G <= 16, page size 16 (else SEGKV_ERR_UNSUPPORTED).
+ */
+int32_t segkv_decode_workspace_size(const segkv_dims* dims, const segkv_meta* meta_host, size_t* bytes);
+int32_t segpaged_attn_decode(const segkv_dims* dims, const segkv_meta* meta_host, const segkv_meta* meta_dev,
+                             const void* q_new, const void* k_new, const void* v_new,
+                             const void* k_pool, const void* v_pool, int64_t pool_pages,
+                             const int32_t* page_indptr_dev, const int32_t* page_ids_dev,
+                             const int32_t* page_pos_dev, float softmax_scale, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * EXECUTE selection (README "About": Elastic Sparsity, token-selective FFN from
  * attention importance; paooo.com "RedKnot的主要功能": top-k tokens by attention
  * score take the dense FFN).

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(hk.LIB_PATH), reason="libsegk
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(segkv_\w+|rope_relocate|segpaged_attn_prefill|token_importance_topk|"
+    return sorted(set(re.findall(r"\b(segkv_\w+|rope_relocate|segpaged_attn_\w+|token_importance_topk|"
                                  r"sparse_ffn_\w+)\s*\(", src)))
 
 
