@@ -57,6 +57,30 @@ def visible_pairs_per_row(w):
     return out
 
 
+def decode_visible_pages(w):
+    """Pages holding a key visible to the decode row (position L_k) of each (r, h): the
+    same closed forms per class, at i = L_k, over the stored keys [0, L_k)."""
+    total = 0
+    for r in range(w.num_requests):
+        sq = w.query_segment(r)
+        bq, Lk = int(w.seg_start[sq]), w.context_len(r)
+        for h in range(w.num_kv_heads):
+            k = r * w.num_kv_heads + h
+            c = int(w.head_class[k])
+            if c in (0, 3):
+                ivs = [(0, Lk)]
+            elif c == 1:
+                ivs = [(max(0, min(bq, Lk - int(w.window[k]) + 1)), Lk)]
+            else:
+                segs = [int(s) for s in w.retr_seg[2 * k:2 * k + 2]]
+                ivs = [(bq, Lk)] + [(int(w.seg_start[s]), int(w.seg_start[s] + w.seg_len[s])) for s in segs]
+            pages = set()
+            for lo, hi in ivs:
+                pages.update(range(lo // 16, (hi + 15) // 16))
+            total += len(pages)
+    return total
+
+
 def profile_traffic(kernel_tag, src_hash):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
@@ -326,6 +350,22 @@ def main():
         del xa, xb, sets
         log(f"relocate full K+V {result['relocate_full_kv']['GB/s']:.0f} GB/s, "
             f"K only {result['relocate_full_k']['GB/s']:.0f} GB/s, copy {result['copy_256MiB_GB/s']:.0f} GB/s")
+
+        # decode step of the same layer: one new row per request over the same page tables
+        dq, dk, dv = (bf16(x) for x in workloads.decode_inputs(w, seed=0))
+        dout = torch.empty(w.num_requests, Hq, D, dtype=torch.bfloat16, device=dev)
+        dlse = torch.empty(w.num_requests, Hq, dtype=torch.float32, device=dev)
+        dgraph = capture(repeat(lambda: layer.decode(dq, dk, dv, k_work, v_work, out=dout, lse=dlse)))
+        t = time_graph(dgraph, 20) / per_graph
+        n_vis = decode_visible_pages(w)
+        n_tab = int(layer.sizes["table_entries"])
+        nbytes = n_vis * 16 * D * 2 * 2.0  # K + V of every page holding a visible key
+        result["decode_32k"] = {
+            "us": t * 1e3, "visible_pages": n_vis, "table_pages_read": n_tab, "bytes": nbytes,
+            "GB/s": nbytes / (t * 1e-3) / 1e9, "pct_hbm_peak": 100.0 * nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "kernels": "decode_main_kernel + decode_combine_kernel",
+            "algorithmic": "K+V of every page holding a key visible to the new row, per kv head"}
+        log(f"decode {t * 1e3:.1f} us, {result['decode_32k']['GB/s']:.0f} GB/s of visible K+V pages")
 
         # sparse SwiGLU FFN of the 8K selection workload (k = 2048 rows, 4096 -> 14336)
         log("generating sparse_ffn_8k FFN inputs")

@@ -182,70 +182,105 @@ __global__ __launch_bounds__(kDecThreads) void decode_main_kernel(DecArgs a) {
   }
 }
 
-// One work-group per (request, query head): merges the runs of its kv head's
-// table and the new token, runs in table order:
+// Work-group (request, query head, 32-dim slice of the head): merges the runs
+// of its kv head's table and the new token:
 //   m* = max(m_new, max_c m_c), L = 2^(m_new - m*) + sum_c 2^(m_c - m*) l_c,
 //   O = (2^(m_new - m*) v_new + sum_c 2^(m_c - m*) O_c) / L, LSE = (m* + log2 L) ln 2,
-// with m_new = scale log2(e) q . k_new.
+// with m_new = scale log2(e) q . k_new. Thread (d, q) adds runs q, q + 32, ...
+// into four accumulators (loads of four runs in flight); the partial sums are
+// combined in a fixed order, so the result does not depend on timing.
+constexpr int kDecCombThreads = 1024;
+constexpr int kDecCombDims = 32;                                // dims per work-group
+constexpr int kDecCombGroups = kDecCombThreads / kDecCombDims;  // run groups
+
+__device__ __forceinline__ float dec_wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ float dec_wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
 template <int D>
-__global__ __launch_bounds__(kDecThreads) void decode_combine_kernel(DecArgs a) {
-  constexpr int NG = kDecThreads / D;  // run groups, summed in a fixed order at the end
-  __shared__ float s_red[kDecThreads];
-  __shared__ float s_acc[NG][D + 1];
+__global__ __launch_bounds__(kDecCombThreads) void decode_combine_kernel(DecArgs a) {
+  constexpr int NG = kDecCombGroups;
+  constexpr int NW = kDecCombThreads / 64;
+  __shared__ float s_wd[NW], s_wm[NW];
+  __shared__ float s_acc[NG][kDecCombDims];
+  __shared__ float s_l[NG];
   const int rg = blockIdx.x, r = rg / a.Hq, gq = rg % a.Hq, h = gq / a.G, g = gq % a.G;
+  const int d0 = blockIdx.y * kDecCombDims;
   const int k = r * a.Hkv + h;
   const int nc = (a.page_indptr[k + 1] - a.page_indptr[k] + kDecChunk - 1) / kDecChunk;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const float* base = a.ws + (size_t)k * a.max_chunks * a.G * (D + 2) + (size_t)g * (D + 2);
   const size_t cstride = (size_t)a.G * (D + 2);
-  // score of the new token against itself, and the largest run max
-  float part = 0.f;
-  for (int d = tid; d < D; d += kDecThreads)
-    part += bf16_bits_to_float(a.q_new[((size_t)r * a.Hq + gq) * D + d]) *
-            bf16_bits_to_float(a.k_new[((size_t)r * a.Hkv + h) * D + d]);
+  // q . k_new over the whole head and the largest run max: wave sums, then waves in order
+  const float prod = tid < D ? bf16_bits_to_float(a.q_new[((size_t)r * a.Hq + gq) * D + tid]) *
+                                   bf16_bits_to_float(a.k_new[((size_t)r * a.Hkv + h) * D + tid])
+                             : 0.f;
   float mx = -INFINITY;
-  for (int cc = tid; cc < nc; cc += kDecThreads) mx = fmaxf(mx, base[cc * cstride + D]);
-  s_red[tid] = part;
-  __syncthreads();
-  if (tid == 0) {
-    float dot = 0.f;
-    for (int t = 0; t < kDecThreads; ++t) dot += s_red[t];
-    s_acc[0][D] = dot * a.scale_log2;
+  for (int cc = tid; cc < nc; cc += kDecCombThreads) mx = fmaxf(mx, base[cc * cstride + D]);
+  const float wd = dec_wave_sum(prod), wm = dec_wave_max(mx);
+  if (lane == 0) {
+    s_wd[wave] = wd;
+    s_wm[wave] = wm;
   }
   __syncthreads();
-  const float m_new = s_acc[0][D];
-  s_red[tid] = mx;
-  __syncthreads();
-  for (int st = kDecThreads / 2; st > 0; st >>= 1) {
-    if (tid < st) s_red[tid] = fmaxf(s_red[tid], s_red[tid + st]);
-    __syncthreads();
+  float dot = 0.f, mruns = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    dot += s_wd[w];
+    mruns = fmaxf(mruns, s_wm[w]);
   }
-  const float mstar = fmaxf(m_new, s_red[0]);
-  __syncthreads();  // every thread has read the max before s_red takes the run sums
-  // weighted sums: thread (d, q) takes runs q, q + NG, ...
-  const int d = tid % D, q = tid / D;
-  float acc = 0.f, lsum = 0.f;
-  for (int cc = q; cc < nc; cc += NG) {
-    const float* sl = base + cc * cstride;
-    const float mc = sl[D];
-    const float wgt = mc == -INFINITY ? 0.f : exp2f(mc - mstar);
-    acc += wgt * sl[d];
-    lsum += wgt * sl[D + 1];
+  const float m_new = dot * a.scale_log2;
+  const float mstar = fmaxf(m_new, mruns);
+  const int dl = tid % kDecCombDims, q = tid / kDecCombDims, d = d0 + dl;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f}, ls[4] = {0.f, 0.f, 0.f, 0.f};
+  int cc = q;
+  for (; cc + 3 * NG < nc; cc += 4 * NG) {
+    float mc[4], lc[4], oc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* sl = base + (cc + u * NG) * cstride;
+      mc[u] = sl[D];
+      lc[u] = sl[D + 1];
+      oc[u] = sl[d];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wgt = mc[u] == -INFINITY ? 0.f : exp2f(mc[u] - mstar);
+      acc[u] += wgt * oc[u];
+      ls[u] += wgt * lc[u];
+    }
   }
-  s_acc[q][d] = acc;
-  if (d == 0) s_red[q] = lsum;  // s_red is free again after the max reduction's last barrier
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {  // at most three runs left
+    if (cc + u * NG < nc) {
+      const float* sl = base + (cc + u * NG) * cstride;
+      const float mc = sl[D];
+      const float wgt = mc == -INFINITY ? 0.f : exp2f(mc - mstar);
+      acc[u] += wgt * sl[d];
+      ls[u] += wgt * sl[D + 1];
+    }
+  }
+  s_acc[q][dl] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  if (dl == 0) s_l[q] = (ls[0] + ls[1]) + (ls[2] + ls[3]);
   __syncthreads();
-  if (tid < D) {
+  if (tid < kDecCombDims) {
     const float wn = exp2f(m_new - mstar);
-    float o = wn * bf16_bits_to_float(a.v_new[((size_t)r * a.Hkv + h) * D + tid]);
+    float o = wn * bf16_bits_to_float(a.v_new[((size_t)r * a.Hkv + h) * D + d0 + tid]);
     float L = wn;
 #pragma unroll
     for (int qq = 0; qq < NG; ++qq) {
       o += s_acc[qq][tid];
-      L += s_red[qq];
+      L += s_l[qq];
     }
-    a.out[((size_t)r * a.Hq + gq) * D + tid] = float_to_bf16_bits(o / L);
-    if (tid == 0 && a.lse != nullptr) a.lse[(size_t)r * a.Hq + gq] = (mstar + log2f(L)) * kDecLn2;
+    a.out[((size_t)r * a.Hq + gq) * D + d0 + tid] = float_to_bf16_bits(o / L);
+    if (tid == 0 && blockIdx.y == 0 && a.lse != nullptr) a.lse[(size_t)r * a.Hq + gq] = (mstar + log2f(L)) * kDecLn2;
   }
 }
 
@@ -339,9 +374,9 @@ extern "C" int32_t segpaged_attn_decode(const segkv_dims* dims, const segkv_meta
     SEGKV_LAUNCH_CHECK();
   }
   if (D == 128)
-    decode_combine_kernel<128><<<a.R * a.Hq, kDecThreads, 0, s>>>(a);
+    decode_combine_kernel<128><<<dim3(a.R * a.Hq, 128 / kDecCombDims), kDecCombThreads, 0, s>>>(a);
   else
-    decode_combine_kernel<64><<<a.R * a.Hq, kDecThreads, 0, s>>>(a);
+    decode_combine_kernel<64><<<dim3(a.R * a.Hq, 64 / kDecCombDims), kDecCombThreads, 0, s>>>(a);
   SEGKV_LAUNCH_CHECK();
   return SEGKV_OK;
 }
