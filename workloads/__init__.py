@@ -63,6 +63,20 @@ def decode_inputs(w, seed: int = 0):
     return (_normal_bf16(rng, (R, Hq, D)), _normal_bf16(rng, (R, Hkv, D)), _normal_bf16(rng, (R, Hkv, D)))
 
 
+
+def layer_inputs(w, hidden_size: int, seed: int = 0):
+    """Inputs of one layer's projections around the attention: the query rows'
+    residual stream and random-init weights. Returns bf16 bit patterns
+    (hidden [T_q, hidden_size] ~ N(0, 1); w_qkv [(Hq + 2 Hkv) D, hidden_size]
+    ~ N(0, 1/hidden_size); w_o [hidden_size, Hq D] ~ N(0, 1/(Hq D))), so every
+    projected value has unit variance. Input recipe only."""
+    rng = np.random.Generator(np.random.PCG64(20_000 + seed))
+    Hq, Hkv, D, T = w.num_q_heads, w.num_kv_heads, w.head_dim, w.total_q_rows
+    hidden = _normal_bf16(rng, (T, hidden_size))
+    w_qkv = _normal_bf16(rng, ((Hq + 2 * Hkv) * D, hidden_size), std=hidden_size ** -0.5)
+    w_o = _normal_bf16(rng, (hidden_size, Hq * D), std=(Hq * D) ** -0.5)
+    return hidden, w_qkv, w_o
+
 @dataclasses.dataclass
 class Workload:
     """One synthetic batch. Arrays holding bf16 data are uint16 bit patterns.
