@@ -25,6 +25,7 @@ EXPORTS = [
     "segkv_visible_spans", "rope_relocate", "segpaged_attn_prefill", "token_importance_topk",
     "segkv_decode_workspace_size", "segpaged_attn_decode",
     "segkv_topk_select", "sparse_ffn_workspace_size", "sparse_ffn_swiglu",
+    "segkv_qkv_workspace_size", "segkv_qkv_rope_append", "segkv_out_proj_residual",
 ]
 
 
@@ -81,6 +82,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "segkv_topk_select": ([P, I32, I32, P, P], I32),
         "sparse_ffn_workspace_size": ([I32, I32], SZ),
         "sparse_ffn_swiglu": ([P, I32, I32, I32, P, I32, P, P, P, P, SZ, P], I32),
+        "segkv_qkv_workspace_size": ([P, P, P], I32),
+        "segkv_qkv_rope_append": ([P, P, P, P, P, P, I64, P, I32, P, F64, P, P, P, P, SZ, P], I32),
+        "segkv_out_proj_residual": ([P, I32, I32, P, P, I32, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -245,3 +249,30 @@ def sparse_ffn_swiglu(hidden, idx, k: int, w_gate, w_up, w_down, workspace, stre
     _check("sparse_ffn_swiglu", lib.sparse_ffn_swiglu(
         _ptr(hidden), n_rows, hidden_size, inter, _ptr(idx), k, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def segkv_qkv_workspace_size(d: Dims, meta: HostMeta) -> int:
+    lib = load()
+    ms = meta.struct()
+    n = ctypes.c_size_t(0)
+    _check("segkv_qkv_workspace_size", lib.segkv_qkv_workspace_size(ctypes.byref(d), ctypes.byref(ms),
+                                                                    ctypes.byref(n)))
+    return int(n.value)
+
+
+def segkv_qkv_rope_append(d: Dims, meta: HostMeta, dmeta: DeviceMeta, cu_q, seg_page_indptr, seg_pages, hidden,
+                          w_qkv, rope_theta: float, q_out, k_pool, v_pool, workspace, stream=None):
+    lib = load()
+    ms, dm = meta.struct(), dmeta.struct()
+    _check("segkv_qkv_rope_append", lib.segkv_qkv_rope_append(
+        ctypes.byref(d), ctypes.byref(ms), ctypes.byref(dm), _ptr(cu_q), _ptr(seg_page_indptr), _ptr(seg_pages),
+        k_pool.shape[0], _ptr(hidden), hidden.shape[1], _ptr(w_qkv), float(rope_theta), _ptr(q_out), _ptr(k_pool),
+        _ptr(v_pool), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def segkv_out_proj_residual(attn, w_o, hidden, stream=None):
+    """attn [n, F] (or [n, Hq, D]), w_o [Hd, F], hidden [n, Hd] updated in place."""
+    lib = load()
+    n, hd = hidden.shape
+    _check("segkv_out_proj_residual", lib.segkv_out_proj_residual(
+        _ptr(attn), n, w_o.shape[1], _ptr(w_o), _ptr(hidden), hd, _stream(stream)))

@@ -11,7 +11,10 @@
 // Both GEMMs compute C^T = W X^T with the gfx950 32x32x16 bf16 MFMA (A = weight
 // rows, B = token rows), so each lane ends up holding one token row and 4-wide
 // runs of output features, which the epilogues store as 8-byte bf16 groups.
+#include <climits>
+
 #include "common.h"
+#include "plan.h"
 
 namespace segkv {
 namespace {
@@ -31,6 +34,56 @@ struct FfnArgs {
   const int32_t* idx;
   int k_tokens, K, out_ld, n_rows;
 };
+
+// Main loop shared by the projections: the work-group's C^T tile (128 weight
+// rows x 128 token rows) over the reduction dimension K, staged through LDS in
+// kBK-deep slices with the next slice's global loads in flight. Thread u-th
+// 16-byte chunks: weight row arow[u], token row brow[u] (NULL: zero row).
+// Wave (wn, wm) accumulates weight rows arow0..+31 (acc[0]) and arow1..+31
+// (acc[1]) against token rows 64 wm..+31 (acc[.][0]) and 64 wm + 32..+63 (acc[.][1]).
+__device__ __forceinline__ void gemm_tile(const uint16_t* const (&arow)[4], const uint16_t* const (&brow)[4],
+                                          const int (&lds_off)[4], int K, int arow0, int arow1, int wm,
+                                          uint16_t* sa, uint16_t* sb, f32x16 (&acc)[2][2]) {
+  const int lane = threadIdx.x & 63, lrow = lane & 31, lg = lane >> 5;
+  u32x4 ra[4], rb[4];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ra[u] = *reinterpret_cast<const u32x4*>(arow[u] + k0);
+      rb[u] = brow[u] ? *reinterpret_cast<const u32x4*>(brow[u] + k0) : u32x4{0, 0, 0, 0};
+    }
+  };
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[x][y][i] = 0.f;
+
+  fetch(0);
+  for (int k0 = 0; k0 < K; k0 += kBK) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      *reinterpret_cast<u32x4*>(&sa[lds_off[u]]) = ra[u];
+      *reinterpret_cast<u32x4*>(&sb[lds_off[u]]) = rb[u];
+    }
+    __syncthreads();
+    if (k0 + kBK < K) fetch(k0 + kBK);
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int col = 16 * ks + 8 * lg;
+      const bf16x8 fa0 = *reinterpret_cast<const bf16x8*>(&sa[(arow0 + lrow) * kLdsStride + col]);
+      const bf16x8 fa1 = *reinterpret_cast<const bf16x8*>(&sa[(arow1 + lrow) * kLdsStride + col]);
+      const bf16x8 fb0 = *reinterpret_cast<const bf16x8*>(&sb[(64 * wm + lrow) * kLdsStride + col]);
+      const bf16x8 fb1 = *reinterpret_cast<const bf16x8*>(&sb[(64 * wm + 32 + lrow) * kLdsStride + col]);
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, fb0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, fb1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, fb0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, fb1, acc[1][1], 0, 0, 0);
+    }
+  }
+}
 
 template <int MODE>
 __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(FfnArgs a) {
@@ -64,49 +117,11 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(FfnArgs a) {
       brow[u] = nullptr;
     }
   }
-  u32x4 ra[4], rb[4];
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ra[u] = *reinterpret_cast<const u32x4*>(arow[u] + k0);
-      rb[u] = brow[u] ? *reinterpret_cast<const u32x4*>(brow[u] + k0) : u32x4{0, 0, 0, 0};
-    }
-  };
-
   // wave's A rows: SwiGLU -> gate block wn and up block wn; residual -> blocks 2wn, 2wn+1
   const int arow0 = MODE == kModeSwiglu ? 32 * wn : 64 * wn;
   const int arow1 = MODE == kModeSwiglu ? 64 + 32 * wn : 64 * wn + 32;
   f32x16 acc[2][2];
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[x][y][i] = 0.f;
-
-  fetch(0);
-  for (int k0 = 0; k0 < a.K; k0 += kBK) {
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      *reinterpret_cast<u32x4*>(&sa[lds_off[u]]) = ra[u];
-      *reinterpret_cast<u32x4*>(&sb[lds_off[u]]) = rb[u];
-    }
-    __syncthreads();
-    if (k0 + kBK < a.K) fetch(k0 + kBK);
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int col = 16 * ks + 8 * lg;
-      const bf16x8 fa0 = *reinterpret_cast<const bf16x8*>(&sa[(arow0 + lrow) * kLdsStride + col]);
-      const bf16x8 fa1 = *reinterpret_cast<const bf16x8*>(&sa[(arow1 + lrow) * kLdsStride + col]);
-      const bf16x8 fb0 = *reinterpret_cast<const bf16x8*>(&sb[(64 * wm + lrow) * kLdsStride + col]);
-      const bf16x8 fb1 = *reinterpret_cast<const bf16x8*>(&sb[(64 * wm + 32 + lrow) * kLdsStride + col]);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, fb0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, fb1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, fb0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, fb1, acc[1][1], 0, 0, 0);
-    }
-  }
+  gemm_tile(arow, brow, lds_off, a.K, arow0, arow1, wm, sa, sb, acc);
 
   // lane holds token row m = m0 + 64 wm + 32 mb + lrow and features 8(i/4) + 4 lg + i%4 of each block
 #pragma unroll
@@ -133,7 +148,7 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(FfnArgs a) {
         *reinterpret_cast<u32x2*>(orow + 8 * g4 + 4 * lg) = u32x2{w[0], w[1]};
       }
     } else {
-      const int dst = a.idx[m];
+      const int dst = a.idx ? a.idx[m] : m;  // no index list: row m itself
       if (dst < 0 || dst >= a.n_rows) continue;  // out-of-range index: row skipped
       uint16_t* orow = a.out + (size_t)dst * a.out_ld + n0;
 #pragma unroll
@@ -156,6 +171,146 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(FfnArgs a) {
           }
           *reinterpret_cast<u32x2*>(p) = u32x2{w[0], w[1]};
         }
+    }
+  }
+}
+
+// ---- layer glue: fused QKV projection + RoPE + append of the query rows' K/V ----
+//
+// paooo.com "如何使用RedKnot" (EXECUTE recomputes the query segment) and RedKnot
+// README "About" (the query segment's KV is produced online into the per-head
+// paged store). Q, K and V of a query row come from one GEMM against the
+// stacked weights [Hq | Hkv | Hkv heads][D rows]; Q and K are rotated at the
+// row's position (rotate-half pairing of dims j and j + D/2, omega_j =
+// theta^(-2j/D)) in the epilogue, which also writes K and V straight into the
+// query segment's working pages. The wave's two weight blocks are chosen so a
+// lane holds both halves of a pair: blocks (32 wn, 64 + 32 wn) of a one-head
+// tile for D = 128, blocks (64 wn, 64 wn + 32) = one head per wave for D = 64.
+
+constexpr int kRowThreads = 64;
+
+struct QkvRowArgs {
+  const int32_t* cu_q;
+  const int32_t* seg_indptr;
+  const int32_t* seg_start;
+  const int32_t* seg_page_indptr;
+  const int32_t* seg_pages;
+  float2* rope_cs;     // [T][D/2] (cos, sin) of row t's angle for pair j
+  int32_t* row_slot;   // [T][Hkv] page * P + slot of row t's K/V for kv head h, or -1
+  int R, T, Hkv, D;
+  int64_t pool_pages;
+  double theta;
+};
+
+// One work-group per query row: its request (largest r with cu_q[r] <= t), its
+// position, the cos/sin of its angles (fp64 sincos, rounded to fp32) and the
+// page slot its K/V go to for each kv head.
+__global__ __launch_bounds__(kRowThreads) void qkv_rows_kernel(QkvRowArgs a) {
+  const int t = blockIdx.x, tid = threadIdx.x;
+  int lo = 0, hi = a.R - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int r = lo, sq = a.seg_indptr[r + 1] - 1, tl = t - a.cu_q[r];
+  const int pos = a.seg_start[sq] + tl;
+  for (int j = tid; j < a.D / 2; j += kRowThreads) {
+    const double w = pow(a.theta, -2.0 * (double)j / (double)a.D);
+    double sn, cn;
+    sincos((double)pos * w, &sn, &cn);
+    a.rope_cs[(size_t)t * (a.D / 2) + j] = make_float2((float)cn, (float)sn);
+  }
+  for (int h = tid; h < a.Hkv; h += kRowThreads) {
+    const int e = a.seg_page_indptr[sq * a.Hkv + h] + tl / kPage;
+    int slot = -1;
+    if (e < a.seg_page_indptr[sq * a.Hkv + h + 1]) {
+      const int page = a.seg_pages[e];
+      if (page >= 0 && page < a.pool_pages) slot = page * kPage + tl % kPage;
+    }
+    a.row_slot[(size_t)t * a.Hkv + h] = slot;
+  }
+}
+
+struct QkvArgs {
+  const uint16_t* w;        // [(Hq + 2 Hkv) D][K]
+  const uint16_t* x;        // [T][K]
+  const float2* rope_cs;
+  const int32_t* row_slot;
+  uint16_t* q_out;          // [T][Hq][D]
+  uint16_t* k_pool;         // [pages][P][D]
+  uint16_t* v_pool;         // [pages][D][P]
+  int T, K, Hq, Hkv, D;
+};
+
+__global__ __launch_bounds__(kFfnThreads, 2) void qkv_rope_append_kernel(QkvArgs a) {
+  __shared__ uint16_t sa[kRowsA * kLdsStride];
+  __shared__ uint16_t sb[kRowsB * kLdsStride];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lrow = lane & 31, lg = lane >> 5;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int n0 = blockIdx.x * kRowsA, m0 = blockIdx.y * kRowsB;
+  const int nfeat = (a.Hq + 2 * a.Hkv) * a.D;
+  const uint16_t* arow[4];
+  const uint16_t* brow[4];
+  int lds_off[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int qd = tid + u * kFfnThreads;
+    const int row = qd >> 3, c = qd & 7;
+    lds_off[u] = row * kLdsStride + 8 * c;
+    const int nrow = n0 + row < nfeat ? n0 + row : nfeat - 1;  // a half tile past the last head (D = 64)
+    arow[u] = a.w + (size_t)nrow * a.K + 8 * c;
+    brow[u] = m0 + row < a.T ? a.x + (size_t)(m0 + row) * a.K + 8 * c : nullptr;
+  }
+  const int arow0 = a.D == 128 ? 32 * wn : 64 * wn;
+  const int arow1 = a.D == 128 ? 64 + 32 * wn : 64 * wn + 32;
+  f32x16 acc[2][2];
+  gemm_tile(arow, brow, lds_off, a.K, arow0, arow1, wm, sa, sb, acc);
+
+  // acc[0][mb][i] and acc[1][mb][i]: dims j and j + D/2 of head `head`, token row m,
+  // with j = j0 + 8 (i/4) + 4 lg + i%4
+  const int head = (n0 + arow0) / a.D, j0 = (n0 + arow0) % a.D, half = a.D / 2;
+  if (head >= a.Hq + 2 * a.Hkv) return;  // the unused half of the last tile
+  const int kind = head < a.Hq ? 0 : head < a.Hq + a.Hkv ? 1 : 2;  // Q, K, V
+  const int hk = kind == 1 ? head - a.Hq : head - a.Hq - a.Hkv;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = m0 + 64 * wm + 32 * mb + lrow;
+    if (m >= a.T) continue;
+    const int slot = kind == 0 ? 0 : a.row_slot[(size_t)m * a.Hkv + hk];
+    if (slot < 0) continue;  // no page for this row: nothing written
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int j = j0 + 8 * g4 + 4 * lg;
+      float lo4[4], hi4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = acc[0][mb][4 * g4 + e], y = acc[1][mb][4 * g4 + e];
+        if (kind == 2) {
+          lo4[e] = x;
+          hi4[e] = y;
+        } else {
+          const float2 cs = a.rope_cs[(size_t)m * half + j + e];
+          lo4[e] = x * cs.x - y * cs.y;
+          hi4[e] = x * cs.y + y * cs.x;
+        }
+      }
+      if (kind == 2) {  // d-major page: element (d, slot) at d * P + slot
+        uint16_t* vp = a.v_pool + (size_t)(slot / kPage) * a.D * kPage + slot % kPage;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vp[(size_t)(j + e) * kPage] = float_to_bf16_bits(lo4[e]);
+          vp[(size_t)(j + e + half) * kPage] = float_to_bf16_bits(hi4[e]);
+        }
+      } else {
+        uint16_t* dst = kind == 0 ? a.q_out + ((size_t)m * a.Hq + head) * a.D : a.k_pool + (size_t)slot * a.D;
+        const u32x2 wl = {(uint32_t)float_to_bf16_bits(lo4[0]) | (uint32_t)float_to_bf16_bits(lo4[1]) << 16,
+                          (uint32_t)float_to_bf16_bits(lo4[2]) | (uint32_t)float_to_bf16_bits(lo4[3]) << 16};
+        const u32x2 wh = {(uint32_t)float_to_bf16_bits(hi4[0]) | (uint32_t)float_to_bf16_bits(hi4[1]) << 16,
+                          (uint32_t)float_to_bf16_bits(hi4[2]) | (uint32_t)float_to_bf16_bits(hi4[3]) << 16};
+        *reinterpret_cast<u32x2*>(dst + j) = wl;
+        *reinterpret_cast<u32x2*>(dst + j + half) = wh;
+      }
     }
   }
 }
@@ -209,6 +364,112 @@ extern "C" int32_t sparse_ffn_swiglu(void* hidden, int32_t n_rows, int32_t hidde
   g2.out_ld = hidden_size;
   g2.n_rows = n_rows;
   ffn_gemm_kernel<kModeResidual><<<dim3(hidden_size / kRowsA, cdiv(k, kRowsB)), kFfnThreads, 0, s>>>(g2);
+  SEGKV_LAUNCH_CHECK();
+  return SEGKV_OK;
+}
+
+namespace {
+size_t qkv_ws_bytes(int64_t T, int Hkv, int D) {
+  const size_t cs = ((size_t)T * (D / 2) * sizeof(float2) + 255) & ~(size_t)255;
+  return cs + (size_t)T * Hkv * sizeof(int32_t);
+}
+}  // namespace
+
+extern "C" int32_t segkv_qkv_workspace_size(const segkv_dims* dims, const segkv_meta* meta_host, size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(SEGKV_ERR_INVALID_ARG, "bytes is NULL");
+  const int32_t st = validate_layout(dims, meta_host);
+  if (st != SEGKV_OK) return st;
+  int64_t T = 0;
+  for (int r = 0; r < dims->num_requests; ++r) T += meta_host->seg_len[meta_host->seg_indptr[r + 1] - 1];
+  *bytes = qkv_ws_bytes(T, dims->num_kv_heads, dims->head_dim);
+  return SEGKV_OK;
+}
+
+extern "C" int32_t segkv_qkv_rope_append(const segkv_dims* dims, const segkv_meta* meta_host,
+                                         const segkv_meta* meta_dev, const int32_t* cu_q_dev,
+                                         const int32_t* seg_page_indptr_dev, const int32_t* seg_pages_dev,
+                                         int64_t pool_pages, const void* hidden, int32_t hidden_size,
+                                         const void* w_qkv, double rope_theta, void* q_out, void* k_pool,
+                                         void* v_pool, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  const int32_t st = validate_layout(dims, meta_host);
+  if (st != SEGKV_OK) return st;
+  const int R = dims->num_requests, Hq = dims->num_q_heads, Hkv = dims->num_kv_heads, D = dims->head_dim;
+  if (!meta_dev || !cu_q_dev || !seg_page_indptr_dev || !seg_pages_dev || !hidden || !w_qkv || !q_out ||
+      !k_pool || !v_pool || !workspace)
+    return fail(SEGKV_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (hidden_size <= 0 || hidden_size % kBK != 0)
+    return fail(SEGKV_ERR_UNSUPPORTED, "hidden_size must be a positive multiple of 64");
+  if (!(rope_theta > 0.0)) return fail(SEGKV_ERR_INVALID_ARG, "rope_theta must be > 0");
+  if (pool_pages <= 0 || pool_pages > INT32_MAX / kPage)
+    return fail(SEGKV_ERR_INVALID_ARG, "pool_pages must be in 1 .. 2^31 / page_size");
+  int64_t T = 0;
+  for (int r = 0; r < R; ++r) T += meta_host->seg_len[meta_host->seg_indptr[r + 1] - 1];
+  if (T > INT32_MAX / 2) return fail(SEGKV_ERR_UNSUPPORTED, "too many query rows");
+  if (workspace_bytes < qkv_ws_bytes(T, Hkv, D))
+    return fail(SEGKV_ERR_WORKSPACE, "workspace smaller than segkv_qkv_workspace_size");
+  if (!aligned16(hidden) || !aligned16(w_qkv) || !aligned16(q_out) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned16(workspace))
+    return fail(SEGKV_ERR_ALIGNMENT, "tensors must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QkvRowArgs ra;
+  ra.cu_q = cu_q_dev;
+  ra.seg_indptr = meta_dev->seg_indptr;
+  ra.seg_start = meta_dev->seg_start;
+  ra.seg_page_indptr = seg_page_indptr_dev;
+  ra.seg_pages = seg_pages_dev;
+  ra.rope_cs = static_cast<float2*>(workspace);
+  ra.row_slot = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                           (((size_t)T * (D / 2) * sizeof(float2) + 255) & ~(size_t)255));
+  ra.R = R;
+  ra.T = (int)T;
+  ra.Hkv = Hkv;
+  ra.D = D;
+  ra.pool_pages = pool_pages;
+  ra.theta = rope_theta;
+  qkv_rows_kernel<<<(unsigned)T, kRowThreads, 0, s>>>(ra);
+  SEGKV_LAUNCH_CHECK();
+  QkvArgs a;
+  a.w = static_cast<const uint16_t*>(w_qkv);
+  a.x = static_cast<const uint16_t*>(hidden);
+  a.rope_cs = ra.rope_cs;
+  a.row_slot = ra.row_slot;
+  a.q_out = static_cast<uint16_t*>(q_out);
+  a.k_pool = static_cast<uint16_t*>(k_pool);
+  a.v_pool = static_cast<uint16_t*>(v_pool);
+  a.T = (int)T;
+  a.K = hidden_size;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  qkv_rope_append_kernel<<<dim3(cdiv((Hq + 2 * Hkv) * D, kRowsA), cdiv((int)T, kRowsB)), kFfnThreads, 0, s>>>(a);
+  SEGKV_LAUNCH_CHECK();
+  return SEGKV_OK;
+}
+
+extern "C" int32_t segkv_out_proj_residual(const void* attn, int32_t n_rows, int32_t in_features, const void* w_o,
+                                           void* hidden, int32_t hidden_size, void* stream) {
+  clear_error();
+  if (n_rows < 0 || in_features <= 0 || hidden_size <= 0)
+    return fail(SEGKV_ERR_INVALID_ARG, "need n_rows >= 0, in_features > 0 and hidden_size > 0");
+  if (in_features % kBK != 0 || hidden_size % kRowsA != 0)
+    return fail(SEGKV_ERR_UNSUPPORTED, "in_features must be a multiple of 64 and hidden_size of 128");
+  if (n_rows == 0) return SEGKV_OK;
+  if (!attn || !w_o || !hidden) return fail(SEGKV_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(attn) || !aligned16(w_o) || !aligned16(hidden))
+    return fail(SEGKV_ERR_ALIGNMENT, "tensors must be 16-byte aligned");
+  FfnArgs g;
+  g.a0 = static_cast<const uint16_t*>(w_o);
+  g.a1 = nullptr;
+  g.x = static_cast<const uint16_t*>(attn);
+  g.out = static_cast<uint16_t*>(hidden);
+  g.idx = nullptr;
+  g.k_tokens = n_rows;
+  g.K = in_features;
+  g.out_ld = hidden_size;
+  g.n_rows = n_rows;
+  ffn_gemm_kernel<kModeResidual><<<dim3(hidden_size / kRowsA, cdiv(n_rows, kRowsB)), kFfnThreads, 0, hipStream_t(stream)>>>(g);
   SEGKV_LAUNCH_CHECK();
   return SEGKV_OK;
 }

@@ -17,7 +17,8 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (HostMeta, dims, rope_relocate, segkv_build_pages, segkv_decode_workspace_size, segkv_plan_sizes,
+from . import (HostMeta, dims, rope_relocate, segkv_build_pages, segkv_decode_workspace_size,
+               segkv_out_proj_residual, segkv_plan_sizes, segkv_qkv_rope_append, segkv_qkv_workspace_size,
                segkv_visible_spans, segpaged_attn_decode, segpaged_attn_prefill, sparse_ffn_swiglu,
                sparse_ffn_workspace_size, token_importance_topk)
 
@@ -100,6 +101,26 @@ class SegPagedLayer:
                              self.page_indptr, self.page_ids, self.page_pos, self.scale, out, lse,
                              self.dec_workspace, stream=stream)
         return out, lse
+
+    def qkv_rope_append(self, hidden, w_qkv, rope_theta: float, seg_page_indptr, seg_pages, k_pool, v_pool,
+                        q_out=None, stream=None):
+        """Query rows' fused QKV projection + RoPE; K/V written into the query
+        segment's working pages. hidden: [T_q][hidden]; returns Q [T_q][Hq][D]."""
+        Hq, D = self.dims.num_q_heads, self.dims.head_dim
+        if q_out is None:
+            q_out = torch.empty(int(self.cu_q_host[-1]), Hq, D, dtype=torch.bfloat16, device=self.device)
+        if not hasattr(self, "qkv_workspace"):
+            nbytes = segkv_qkv_workspace_size(self.dims, self.meta)
+            self.qkv_workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.device)
+        segkv_qkv_rope_append(self.dims, self.meta, self.dmeta, self.cu_q, seg_page_indptr, seg_pages, hidden,
+                              w_qkv, rope_theta, q_out, k_pool, v_pool, self.qkv_workspace, stream=stream)
+        return q_out
+
+    @staticmethod
+    def out_proj_residual(attn, w_o, hidden, stream=None):
+        """hidden += W_o . attn per row, in place (attn: [T_q][Hq][D] or [T_q][Hq*D])."""
+        segkv_out_proj_residual(attn, w_o, hidden, stream=stream)
+        return hidden
 
     def importance_topk(self, q, k_pool, lse, n_last: int, k: Optional[Sequence[int]], importance=None,
                         topk_idx=None, stream=None):

@@ -265,6 +265,49 @@ int32_t sparse_ffn_swiglu(void* hidden, int32_t n_rows, int32_t hidden_size, int
                           const int32_t* idx_dev, int32_t k, const void* w_gate, const void* w_up,
                           const void* w_down, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Layer glue before the attention: the query segment's fused QKV projection,
+ * RoPE at the rows' positions and the online append of their K/V into the
+ * query segment's working pages (paooo.com "如何使用RedKnot": EXECUTE
+ * recomputes the query segment; RedKnot README "About": the query segment's
+ * KV is produced online into the per-head paged store).
+ * Row t of request r (rows cu_q[r] .. cu_q[r+1]-1, cu_q as for
+ * segkv_build_pages) sits at position p = b_q(r) + t - cu_q[r]. With
+ * y = W_qkv . hidden[t] (fp32 accumulation) split into Hq query heads, then Hkv
+ * key heads, then Hkv value heads of D values each:
+ *   q_out[t][g]           = bf16(rope(y_q[g], p))
+ *   K of (t, h)           = bf16(rope(y_k[h], p)) at page seg_pages[seg_page_indptr[s_q*Hkv+h] + (t-cu_q[r])/16],
+ *                           slot (t-cu_q[r]) % 16 (k_pool token-major [pages][P][D])
+ *   V of (t, h)           = bf16(y_v[h]) at the same page and slot (v_pool d-major [pages][D][P])
+ * rope: rotate-half pairs (j, j + D/2) turned by p * rope_theta^(-2j/D), the
+ * angle's cos/sin taken in fp64 and rounded to fp32. Rows whose page index
+ * falls outside the segment's page run or the pool are not written.
+ * hidden: [T_q][hidden_size] bf16; w_qkv: [(Hq + 2 Hkv) * D][hidden_size] bf16
+ * (row-major, out_features first); q_out: [T_q][Hq][D] bf16. Every other pool
+ * page is left untouched. workspace: segkv_qkv_workspace_size bytes (a
+ * per-row cos/sin table and page-slot list).
+ * Limits: hidden_size a multiple of 64 (else SEGKV_ERR_UNSUPPORTED).
+ */
+int32_t segkv_qkv_workspace_size(const segkv_dims* dims, const segkv_meta* meta_host, size_t* bytes);
+int32_t segkv_qkv_rope_append(const segkv_dims* dims, const segkv_meta* meta_host, const segkv_meta* meta_dev,
+                              const int32_t* cu_q_dev, const int32_t* seg_page_indptr_dev,
+                              const int32_t* seg_pages_dev, int64_t pool_pages, const void* hidden,
+                              int32_t hidden_size, const void* w_qkv, double rope_theta, void* q_out,
+                              void* k_pool, void* v_pool, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Layer glue after the attention: the output projection added onto the
+ * residual stream, in place (the attention half of the layer that EXECUTE
+ * runs, paooo.com "如何使用RedKnot"):
+ *   hidden[t] <- bf16( hidden[t] + W_o . attn[t] ),  t < n_rows, fp32 accumulation.
+ * attn: [n_rows][in_features] bf16 (the attention output [T_q][Hq][D] is
+ * in_features = Hq * D); w_o: [hidden_size][in_features] bf16; hidden:
+ * [n_rows][hidden_size] bf16. Limits: in_features a multiple of 64,
+ * hidden_size a multiple of 128 (else SEGKV_ERR_UNSUPPORTED).
+ */
+int32_t segkv_out_proj_residual(const void* attn, int32_t n_rows, int32_t in_features, const void* w_o,
+                                void* hidden, int32_t hidden_size, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
