@@ -367,6 +367,30 @@ def main():
             "algorithmic": "K+V of every page holding a key visible to the new row, per kv head"}
         log(f"decode {t * 1e3:.1f} us, {result['decode_32k']['GB/s']:.0f} GB/s of visible K+V pages")
 
+        # the layer glue around the attention: fused QKV projection + RoPE + append, output projection
+        log("generating layer weights (hidden 4096)")
+        hs = 4096
+        lh, lwqkv, lwo = (bf16(x) for x in workloads.layer_inputs(w, hs, seed=0))
+        lq = torch.empty(T, Hq, D, dtype=torch.bfloat16, device=dev)
+        seg_pi, seg_pg = i32(w.seg_page_indptr), i32(w.seg_pages)
+        qgraph = capture(repeat(lambda: layer.qkv_rope_append(lh, lwqkv, w.rope_theta, seg_pi, seg_pg, k_work,
+                                                              v_work, q_out=lq)))
+        t_qkv = time_graph(qgraph, 20) / per_graph
+        attn_rows = torch.empty(T, Hq * D, dtype=torch.bfloat16, device=dev).normal_()
+        ograph = capture(repeat(lambda: layer.out_proj_residual(attn_rows, lwo, lh)))
+        t_out = time_graph(ograph, 20) / per_graph
+        qkv_flops = 2.0 * T * hs * (Hq + 2 * w.num_kv_heads) * D
+        out_flops = 2.0 * T * hs * Hq * D
+        result["layer_glue_32k"] = {
+            "hidden": hs, "rows": T,
+            "qkv_rope_append_us": t_qkv * 1e3, "qkv_tflops": qkv_flops / (t_qkv * 1e-3) / 1e12,
+            "out_proj_us": t_out * 1e3, "out_proj_tflops": out_flops / (t_out * 1e-3) / 1e12,
+            "layer_us": (t_qkv + t_pages + t_reloc + t_attn + t_out) * 1e3,
+            "layer": "qkv_rope_append + build_pages + rope_relocate + segpaged_attn_prefill + out_proj_residual"}
+        log(f"layer glue: qkv {t_qkv * 1e3:.1f} us ({result['layer_glue_32k']['qkv_tflops']:.0f} TFLOP/s), "
+            f"out_proj {t_out * 1e3:.1f} us ({result['layer_glue_32k']['out_proj_tflops']:.0f} TFLOP/s)")
+        del lh, lwqkv, lwo, qgraph, ograph
+
         # sparse SwiGLU FFN of the 8K selection workload (k = 2048 rows, 4096 -> 14336)
         log("generating sparse_ffn_8k FFN inputs")
         w5 = workloads.sparse_ffn_8k()

@@ -37,55 +37,74 @@ struct FfnArgs {
 
 // Main loop shared by the projections: the work-group's C^T tile (128 weight
 // rows x 128 token rows) over the reduction dimension K, staged through LDS in
-// kBK-deep slices with the next slice's global loads in flight. Thread u-th
+// kBK-deep slices, each slice's global loads issued kStages slices ahead. Thread u-th
 // 16-byte chunks: weight row arow[u], token row brow[u] (NULL: zero row).
 // Wave (wn, wm) accumulates weight rows arow0..+31 (acc[0]) and arow1..+31
-// (acc[1]) against token rows 64 wm..+31 (acc[.][0]) and 64 wm + 32..+63 (acc[.][1]).
-__device__ __forceinline__ void gemm_tile(const uint16_t* const (&arow)[4], const uint16_t* const (&brow)[4],
+// (acc[1]) against NB blocks of 32 token rows from 32 NB wm (acc[.][b]); the
+// token tile is 64 NB rows (NB = 1 halves it, doubling the work-groups of a
+// launch with few token rows).
+template <int NB>
+__device__ __forceinline__ void gemm_tile(const uint16_t* const (&arow)[4], const uint16_t* const (&brow)[2 * NB],
                                           const int (&lds_off)[4], int K, int arow0, int arow1, int wm,
-                                          uint16_t* sa, uint16_t* sb, f32x16 (&acc)[2][2]) {
+                                          uint16_t* sa, uint16_t* sb, f32x16 (&acc)[2][NB]) {
   const int lane = threadIdx.x & 63, lrow = lane & 31, lg = lane >> 5;
-  u32x4 ra[4], rb[4];
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ra[u] = *reinterpret_cast<const u32x4*>(arow[u] + k0);
-      rb[u] = brow[u] ? *reinterpret_cast<const u32x4*>(brow[u] + k0) : u32x4{0, 0, 0, 0};
-    }
-  };
+  // a ring of kStages register sets: slice k is loaded kStages slices ahead of
+  // its use. The 64-row token tile (fewer waves per CU's worth of work) takes
+  // three; the 128-row tile keeps one, as more stages cost it occupancy.
+  constexpr int kStages = NB == 1 ? 3 : 1;
+  u32x4 ra[kStages][4], rb[kStages][2 * NB];
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+    for (int y = 0; y < NB; ++y)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[x][y][i] = 0.f;
-
-  fetch(0);
-  for (int k0 = 0; k0 < K; k0 += kBK) {
-    __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      *reinterpret_cast<u32x4*>(&sa[lds_off[u]]) = ra[u];
-      *reinterpret_cast<u32x4*>(&sb[lds_off[u]]) = rb[u];
+  for (int st = 0; st < kStages; ++st)
+    if (st * kBK < K) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ra[st][u] = *reinterpret_cast<const u32x4*>(arow[u] + st * kBK);
+#pragma unroll
+      for (int u = 0; u < 2 * NB; ++u)
+        rb[st][u] = brow[u] ? *reinterpret_cast<const u32x4*>(brow[u] + st * kBK) : u32x4{0, 0, 0, 0};
     }
-    __syncthreads();
-    if (k0 + kBK < K) fetch(k0 + kBK);
+  for (int k0 = 0; k0 < K; k0 += kStages * kBK) {
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int col = 16 * ks + 8 * lg;
-      const bf16x8 fa0 = *reinterpret_cast<const bf16x8*>(&sa[(arow0 + lrow) * kLdsStride + col]);
-      const bf16x8 fa1 = *reinterpret_cast<const bf16x8*>(&sa[(arow1 + lrow) * kLdsStride + col]);
-      const bf16x8 fb0 = *reinterpret_cast<const bf16x8*>(&sb[(64 * wm + lrow) * kLdsStride + col]);
-      const bf16x8 fb1 = *reinterpret_cast<const bf16x8*>(&sb[(64 * wm + 32 + lrow) * kLdsStride + col]);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, fb0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, fb1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, fb0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, fb1, acc[1][1], 0, 0, 0);
+    for (int st = 0; st < kStages; ++st) {
+      const int kk = k0 + st * kBK;
+      if (kk >= K) break;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(&sa[lds_off[u]]) = ra[st][u];
+#pragma unroll
+      for (int u = 0; u < 2 * NB; ++u) *reinterpret_cast<u32x4*>(&sb[lds_off[u]]) = rb[st][u];
+      __syncthreads();
+      const int kn = kk + kStages * kBK;
+      if (kn < K) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ra[st][u] = *reinterpret_cast<const u32x4*>(arow[u] + kn);
+#pragma unroll
+        for (int u = 0; u < 2 * NB; ++u)
+          rb[st][u] = brow[u] ? *reinterpret_cast<const u32x4*>(brow[u] + kn) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int ks = 0; ks < kBK / 16; ++ks) {
+        const int col = 16 * ks + 8 * lg;
+        const bf16x8 fa0 = *reinterpret_cast<const bf16x8*>(&sa[(arow0 + lrow) * kLdsStride + col]);
+        const bf16x8 fa1 = *reinterpret_cast<const bf16x8*>(&sa[(arow1 + lrow) * kLdsStride + col]);
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          const bf16x8 fb =
+              *reinterpret_cast<const bf16x8*>(&sb[(32 * NB * wm + 32 * bb + lrow) * kLdsStride + col]);
+          acc[0][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, fb, acc[0][bb], 0, 0, 0);
+          acc[1][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, fb, acc[1][bb], 0, 0, 0);
+        }
+      }
     }
   }
 }
 
-template <int MODE>
+template <int MODE, int NB>
 __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(FfnArgs a) {
   __shared__ uint16_t sa[kRowsA * kLdsStride];
   __shared__ uint16_t sb[kRowsB * kLdsStride];
@@ -94,11 +113,11 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(FfnArgs a) {
   const int wn = wave & 1, wm = wave >> 1;
   // SwiGLU: a block covers 64 activation features (gate rows 0..63, up rows 64..127 of the A tile)
   const int n0 = blockIdx.x * (MODE == kModeSwiglu ? 64 : kRowsA);
-  const int m0 = blockIdx.y * kRowsB;
+  const int m0 = blockIdx.y * 64 * NB;
 
-  // source rows of this thread's 16-byte loads (4 A chunks + 4 B chunks per stage)
+  // source rows of this thread's 16-byte loads (4 A chunks + 2 NB B chunks per stage)
   const uint16_t* arow[4];
-  const uint16_t* brow[4];
+  const uint16_t* brow[2 * NB];
   int lds_off[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -109,6 +128,7 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(FfnArgs a) {
       arow[u] = (row < 64 ? a.a0 + (size_t)(n0 + row) * a.K : a.a1 + (size_t)(n0 + row - 64) * a.K) + 8 * c;
     else
       arow[u] = a.a0 + (size_t)(n0 + row) * a.K + 8 * c;
+    if (u >= 2 * NB) continue;
     const int m = m0 + row;
     const int src = m < a.k_tokens ? (MODE == kModeSwiglu ? a.idx[m] : m) : -1;
     if (src >= 0 && (MODE != kModeSwiglu || src < a.n_rows)) {
@@ -120,13 +140,13 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(FfnArgs a) {
   // wave's A rows: SwiGLU -> gate block wn and up block wn; residual -> blocks 2wn, 2wn+1
   const int arow0 = MODE == kModeSwiglu ? 32 * wn : 64 * wn;
   const int arow1 = MODE == kModeSwiglu ? 64 + 32 * wn : 64 * wn + 32;
-  f32x16 acc[2][2];
-  gemm_tile(arow, brow, lds_off, a.K, arow0, arow1, wm, sa, sb, acc);
+  f32x16 acc[2][NB];
+  gemm_tile<NB>(arow, brow, lds_off, a.K, arow0, arow1, wm, sa, sb, acc);
 
-  // lane holds token row m = m0 + 64 wm + 32 mb + lrow and features 8(i/4) + 4 lg + i%4 of each block
+  // lane holds token row m = m0 + 32 NB wm + 32 mb + lrow and features 8(i/4) + 4 lg + i%4 of each block
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int m = m0 + 64 * wm + 32 * mb + lrow;
+  for (int mb = 0; mb < NB; ++mb) {
+    const int m = m0 + 32 * NB * wm + 32 * mb + lrow;
     if (m >= a.k_tokens) continue;
     if (MODE == kModeSwiglu) {
       uint16_t* orow = a.out + (size_t)m * a.out_ld + n0 + 32 * wn;
@@ -242,16 +262,17 @@ struct QkvArgs {
   int T, K, Hq, Hkv, D;
 };
 
+template <int NB>
 __global__ __launch_bounds__(kFfnThreads, 2) void qkv_rope_append_kernel(QkvArgs a) {
   __shared__ uint16_t sa[kRowsA * kLdsStride];
   __shared__ uint16_t sb[kRowsB * kLdsStride];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lrow = lane & 31, lg = lane >> 5;
   const int wn = wave & 1, wm = wave >> 1;
-  const int n0 = blockIdx.x * kRowsA, m0 = blockIdx.y * kRowsB;
+  const int n0 = blockIdx.x * kRowsA, m0 = blockIdx.y * 64 * NB;
   const int nfeat = (a.Hq + 2 * a.Hkv) * a.D;
   const uint16_t* arow[4];
-  const uint16_t* brow[4];
+  const uint16_t* brow[2 * NB];
   int lds_off[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -260,12 +281,12 @@ __global__ __launch_bounds__(kFfnThreads, 2) void qkv_rope_append_kernel(QkvArgs
     lds_off[u] = row * kLdsStride + 8 * c;
     const int nrow = n0 + row < nfeat ? n0 + row : nfeat - 1;  // a half tile past the last head (D = 64)
     arow[u] = a.w + (size_t)nrow * a.K + 8 * c;
-    brow[u] = m0 + row < a.T ? a.x + (size_t)(m0 + row) * a.K + 8 * c : nullptr;
+    if (u < 2 * NB) brow[u] = m0 + row < a.T ? a.x + (size_t)(m0 + row) * a.K + 8 * c : nullptr;
   }
   const int arow0 = a.D == 128 ? 32 * wn : 64 * wn;
   const int arow1 = a.D == 128 ? 64 + 32 * wn : 64 * wn + 32;
-  f32x16 acc[2][2];
-  gemm_tile(arow, brow, lds_off, a.K, arow0, arow1, wm, sa, sb, acc);
+  f32x16 acc[2][NB];
+  gemm_tile<NB>(arow, brow, lds_off, a.K, arow0, arow1, wm, sa, sb, acc);
 
   // acc[0][mb][i] and acc[1][mb][i]: dims j and j + D/2 of head `head`, token row m,
   // with j = j0 + 8 (i/4) + 4 lg + i%4
@@ -274,8 +295,8 @@ __global__ __launch_bounds__(kFfnThreads, 2) void qkv_rope_append_kernel(QkvArgs
   const int kind = head < a.Hq ? 0 : head < a.Hq + a.Hkv ? 1 : 2;  // Q, K, V
   const int hk = kind == 1 ? head - a.Hq : head - a.Hq - a.Hkv;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int m = m0 + 64 * wm + 32 * mb + lrow;
+  for (int mb = 0; mb < NB; ++mb) {
+    const int m = m0 + 32 * NB * wm + 32 * mb + lrow;
     if (m >= a.T) continue;
     const int slot = kind == 0 ? 0 : a.row_slot[(size_t)m * a.Hkv + hk];
     if (slot < 0) continue;  // no page for this row: nothing written
@@ -351,7 +372,7 @@ extern "C" int32_t sparse_ffn_swiglu(void* hidden, int32_t n_rows, int32_t hidde
   g1.K = hidden_size;
   g1.out_ld = inter;
   g1.n_rows = n_rows;
-  ffn_gemm_kernel<kModeSwiglu><<<dim3(inter / 64, cdiv(k, kRowsB)), kFfnThreads, 0, s>>>(g1);
+  ffn_gemm_kernel<kModeSwiglu, 2><<<dim3(inter / 64, cdiv(k, kRowsB)), kFfnThreads, 0, s>>>(g1);
   SEGKV_LAUNCH_CHECK();
   FfnArgs g2;
   g2.a0 = static_cast<const uint16_t*>(w_down);
@@ -363,12 +384,16 @@ extern "C" int32_t sparse_ffn_swiglu(void* hidden, int32_t n_rows, int32_t hidde
   g2.K = inter;
   g2.out_ld = hidden_size;
   g2.n_rows = n_rows;
-  ffn_gemm_kernel<kModeResidual><<<dim3(hidden_size / kRowsA, cdiv(k, kRowsB)), kFfnThreads, 0, s>>>(g2);
+  ffn_gemm_kernel<kModeResidual, 2><<<dim3(hidden_size / kRowsA, cdiv(k, kRowsB)), kFfnThreads, 0, s>>>(g2);
   SEGKV_LAUNCH_CHECK();
   return SEGKV_OK;
 }
 
 namespace {
+// 128-row token tiles leave CUs idle when a launch has fewer than two
+// work-groups per CU (256 CUs); 64-row tiles double the count.
+bool small_grid(int n_tiles, int rows) { return (int64_t)n_tiles * cdiv(rows, kRowsB) < 512; }
+
 size_t qkv_ws_bytes(int64_t T, int Hkv, int D) {
   const size_t cs = ((size_t)T * (D / 2) * sizeof(float2) + 255) & ~(size_t)255;
   return cs + (size_t)T * Hkv * sizeof(int32_t);
@@ -443,7 +468,11 @@ extern "C" int32_t segkv_qkv_rope_append(const segkv_dims* dims, const segkv_met
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.D = D;
-  qkv_rope_append_kernel<<<dim3(cdiv((Hq + 2 * Hkv) * D, kRowsA), cdiv((int)T, kRowsB)), kFfnThreads, 0, s>>>(a);
+  const int nx = cdiv((Hq + 2 * Hkv) * D, kRowsA);
+  if (small_grid(nx, (int)T))
+    qkv_rope_append_kernel<1><<<dim3(nx, cdiv((int)T, 64)), kFfnThreads, 0, s>>>(a);
+  else
+    qkv_rope_append_kernel<2><<<dim3(nx, cdiv((int)T, kRowsB)), kFfnThreads, 0, s>>>(a);
   SEGKV_LAUNCH_CHECK();
   return SEGKV_OK;
 }
@@ -469,7 +498,11 @@ extern "C" int32_t segkv_out_proj_residual(const void* attn, int32_t n_rows, int
   g.K = in_features;
   g.out_ld = hidden_size;
   g.n_rows = n_rows;
-  ffn_gemm_kernel<kModeResidual><<<dim3(hidden_size / kRowsA, cdiv(n_rows, kRowsB)), kFfnThreads, 0, hipStream_t(stream)>>>(g);
+  const int nx = hidden_size / kRowsA;
+  if (small_grid(nx, n_rows))
+    ffn_gemm_kernel<kModeResidual, 1><<<dim3(nx, cdiv(n_rows, 64)), kFfnThreads, 0, hipStream_t(stream)>>>(g);
+  else
+    ffn_gemm_kernel<kModeResidual, 2><<<dim3(nx, cdiv(n_rows, kRowsB)), kFfnThreads, 0, hipStream_t(stream)>>>(g);
   SEGKV_LAUNCH_CHECK();
   return SEGKV_OK;
 }

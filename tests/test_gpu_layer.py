@@ -78,7 +78,17 @@ def test_qkv_mistral_32k():
     _qkv_case(workloads.mistral_32k(), 4096, seed=2)
 
 
-@pytest.mark.parametrize("n_rows,in_f,hd", [(1, 64, 128), (77, 256, 384), (300, 1024, 512), (512, 4096, 4096)])
+def test_qkv_many_rows():
+    # 48 feature tiles x 11 token tiles of 128 rows: the launch takes the 128-row token tile
+    G_, L_ = workloads.GLOBAL, workloads.LOCAL
+    w = workloads.make_custom("rows_1400", Hq=32, Hkv=8, D=128, theta=1e6, seg_lens_per_req=[[64, 1400]],
+                              orig_starts_per_req=[[7, None]], classes=[G_] + [L_] * 7, windows=[0] + [300] * 7)
+    _qkv_case(w, 256, seed=4)
+
+
+# the last two take the 128-row token tile (>= 512 work-groups), the others the 64-row one
+@pytest.mark.parametrize("n_rows,in_f,hd", [(1, 64, 128), (77, 256, 384), (300, 1024, 512), (512, 4096, 4096),
+                                            (2048, 128, 4096), (2050, 64, 4096)])
 def test_out_proj(n_rows, in_f, hd):
     print(f"case out_proj n={n_rows} in={in_f} hidden={hd}", flush=True)
     rng = np.random.Generator(np.random.PCG64(n_rows))
