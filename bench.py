@@ -391,6 +391,58 @@ def main():
             f"out_proj {t_out * 1e3:.1f} us ({result['layer_glue_32k']['out_proj_tflops']:.0f} TFLOP/s)")
         del lh, lwqkv, lwo, qgraph, ograph
 
+        # masked-dense comparator: the same attention over a dense per-head layout with an explicit mask
+        from head_aware_paged_amd import masked_dense_attn, segkv_masked_dense_workspace_size
+        Hkv = w.num_kv_heads
+        L = -(-w.context_len(0) // 64) * 64
+        kd = np.zeros((Hkv, L, D), np.uint16)
+        vd = np.zeros((Hkv, L, D), np.uint16)
+        for h in range(Hkv):
+            for s in w.segments_of(0):
+                b, n = int(w.seg_start[s]), int(w.seg_len[s])
+                run = w.seg_pages[w.seg_page_indptr[s * Hkv + h]:w.seg_page_indptr[s * Hkv + h + 1]]
+                kd[h, b:b + n] = w.k_work[run].reshape(-1, D)[:n]
+                vd[h, b:b + n] = w.v_work[run].reshape(-1, D)[:n]
+        kd_t = bf16(kd)
+        vdt_t = bf16(np.ascontiguousarray(np.swapaxes(vd, 1, 2)))
+        del kd, vd
+        spans = layer.visible_spans().permute(1, 0, 2, 3)  # [Hkv][T][3][(lo, hi)], (-1, -1) padded
+        jj = torch.arange(L, device=dev, dtype=torch.int32)
+        dmask = torch.zeros(Hkv, T, L, dtype=torch.bool, device=dev)
+        for x in range(3):
+            lo, hi = spans[..., x, 0:1], spans[..., x, 1:2]
+            dmask |= (jj >= lo) & (jj < hi)
+        dmask = dmask.to(torch.uint8)
+        dws = torch.empty(segkv_masked_dense_workspace_size(T, Hq, Hkv, D, L), dtype=torch.uint8, device=dev)
+        dout = torch.empty(T, Hq, D, dtype=torch.bfloat16, device=dev)
+        dlse = torch.empty(T, Hq, dtype=torch.float32, device=dev)
+        mgraph = capture(repeat(lambda: masked_dense_attn(q, kd_t, vdt_t, dmask, layer.scale, dout, dlse, dws)))
+        t_dense = time_graph(mgraph, 3) / per_graph
+        dense_flops = 4.0 * D * T * Hq * L
+        result["masked_dense_32k"] = {
+            "us": t_dense * 1e3, "keys": L, "dense_tflops": dense_flops / (t_dense * 1e-3) / 1e12,
+            "mask_bytes": Hkv * T * L, "segpaged_attn_us": t_attn * 1e3, "penalty": t_dense / t_attn,
+            "kernels": "dense_main_kernel + dense_combine_kernel"}
+        log(f"masked dense {t_dense * 1e3:.1f} us ({result['masked_dense_32k']['dense_tflops']:.0f} TFLOP/s dense), "
+            f"{t_dense / t_attn:.2f}x the SegPaged attention")
+        del kd_t, vdt_t, dws, mgraph
+        # the tuned attention kernel in mask mode over all-global (dense) page tables
+        from head_aware_paged_amd.session import SegPagedLayer
+        glayer = SegPagedLayer(Hq, Hkv, D, w.seg_indptr, w.seg_start, w.seg_len, np.zeros_like(w.head_class),
+                               np.zeros_like(w.window), np.full_like(w.retr_seg, -1), page_size=16, device=dev)
+        glayer.build_pages(seg_pi, seg_pg)
+        ggraph = capture(repeat(lambda: glayer.attention_masked(q, k_work, v_work, dmask, out=dout, lse=dlse)))
+        t_gm = time_graph(ggraph, 5) / per_graph
+        dense_pairs = 0
+        for h in range(Hkv):  # every key of every computed tile: rows x keys up to the row's m-tile end
+            dense_pairs += w.num_q_heads // Hkv * T * w.context_len(0)
+        result["masked_dense_tuned_32k"] = {
+            "us": t_gm * 1e3, "dense_tflops": 4.0 * D * dense_pairs / (t_gm * 1e-3) / 1e12,
+            "segpaged_attn_us": t_attn * 1e3, "penalty": t_gm / t_attn,
+            "kernels": "attn_main_kernel<D, true> + attn_combine_kernel over all-global page tables"}
+        log(f"masked dense (tuned kernel, mask mode) {t_gm * 1e3:.1f} us, {t_gm / t_attn:.2f}x the SegPaged attention")
+        del dmask, ggraph, glayer
+
         # sparse SwiGLU FFN of the 8K selection workload (k = 2048 rows, 4096 -> 14336)
         log("generating sparse_ffn_8k FFN inputs")
         w5 = workloads.sparse_ffn_8k()

@@ -22,10 +22,12 @@ GLOBAL, LOCAL, RETRIEVAL, DENSE = 0, 1, 2, 3
 
 EXPORTS = [
     "segkv_status_string", "segkv_last_error", "segkv_plan_sizes", "segkv_build_pages",
-    "segkv_visible_spans", "rope_relocate", "segpaged_attn_prefill", "token_importance_topk",
+    "segkv_visible_spans", "rope_relocate", "segpaged_attn_prefill", "segpaged_attn_prefill_masked",
+    "token_importance_topk",
     "segkv_decode_workspace_size", "segpaged_attn_decode",
     "segkv_topk_select", "sparse_ffn_workspace_size", "sparse_ffn_swiglu",
     "segkv_qkv_workspace_size", "segkv_qkv_rope_append", "segkv_out_proj_residual",
+    "segkv_masked_dense_workspace_size", "masked_dense_attn",
 ]
 
 
@@ -76,6 +78,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "segkv_visible_spans": ([P, P, P, P, P, P], I32),
         "rope_relocate": ([P, P, P, P, I64, I64, P, P, P, I32, I32, I32, F64, P], I32),
         "segpaged_attn_prefill": ([P, P, P, P, P, I64, P, P, P, SZ, F32, P, P, P, SZ, P], I32),
+        "segpaged_attn_prefill_masked": ([P, P, P, P, P, I64, P, P, P, SZ, F32, P, I64, P, P, P, SZ, P], I32),
         "segkv_decode_workspace_size": ([P, P, P], I32),
         "segpaged_attn_decode": ([P, P, P, P, P, P, P, P, I64, P, P, P, F32, P, P, P, SZ, P], I32),
         "token_importance_topk": ([P, P, P, P, P, P, I64, P, P, P, P, SZ, P, F32, I32, P, P, P, P, SZ, P], I32),
@@ -85,6 +88,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "segkv_qkv_workspace_size": ([P, P, P], I32),
         "segkv_qkv_rope_append": ([P, P, P, P, P, P, I64, P, I32, P, F64, P, P, P, P, SZ, P], I32),
         "segkv_out_proj_residual": ([P, I32, I32, P, P, I32, P], I32),
+        "segkv_masked_dense_workspace_size": ([I32, I32, I32, I32, I32, P], I32),
+        "masked_dense_attn": ([P, P, P, P, I32, I32, I32, I32, I32, F32, P, P, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -276,3 +281,34 @@ def segkv_out_proj_residual(attn, w_o, hidden, stream=None):
     n, hd = hidden.shape
     _check("segkv_out_proj_residual", lib.segkv_out_proj_residual(
         _ptr(attn), n, w_o.shape[1], _ptr(w_o), _ptr(hidden), hd, _stream(stream)))
+
+
+def segkv_masked_dense_workspace_size(T: int, Hq: int, Hkv: int, D: int, L: int) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    _check("segkv_masked_dense_workspace_size", lib.segkv_masked_dense_workspace_size(T, Hq, Hkv, D, L,
+                                                                                      ctypes.byref(n)))
+    return int(n.value)
+
+
+def masked_dense_attn(q, k, v_t, mask, softmax_scale: float, out, lse=None, workspace=None, stream=None):
+    """q [T][Hq][D], k [Hkv][L][D], v_t [Hkv][D][L], mask [Hkv][T][L] (uint8)."""
+    lib = load()
+    T, Hq, D = q.shape
+    Hkv, L = k.shape[0], k.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("masked_dense_attn", lib.masked_dense_attn(
+        _ptr(q), _ptr(k), _ptr(v_t), _ptr(mask), T, Hq, Hkv, D, L, float(softmax_scale), _ptr(out), _ptr(lse),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def segpaged_attn_prefill_masked(d: Dims, meta: HostMeta, q, k_pool, v_pool, page_ids, page_pos, plan,
+                                 softmax_scale: float, mask, out, lse=None, workspace=None, stream=None):
+    """mask: [Hkv][T_q][mask_L] uint8 device tensor."""
+    lib = load()
+    ms = meta.struct()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("segpaged_attn_prefill_masked", lib.segpaged_attn_prefill_masked(
+        ctypes.byref(d), ctypes.byref(ms), _ptr(q), _ptr(k_pool), _ptr(v_pool), k_pool.shape[0], _ptr(page_ids),
+        _ptr(page_pos), _ptr(plan), plan.numel() * plan.element_size(), float(softmax_scale), _ptr(mask),
+        mask.shape[-1], _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))

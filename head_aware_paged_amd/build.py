@@ -7,7 +7,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsegkv.so")
-SOURCES = ["host.hip", "pages.hip", "relocate.hip", "attention.hip", "decode.hip", "importance.hip", "ffn.hip"]
+SOURCES = ["host.hip", "pages.hip", "relocate.hip", "attention.hip", "decode.hip", "importance.hip", "ffn.hip",
+           "dense.hip"]
 
 
 def hipcc() -> str:

@@ -58,6 +58,8 @@ struct AttnArgs {
   const uint16_t* zero_page;  // device address of g_zero_page
   float scale_log2;  // softmax_scale * log2(e)
   int Hq, G;
+  const uint8_t* mask;  // explicit mask [Hkv][mask_rows][mask_L] (mask mode only)
+  int64_t mask_rows, mask_L;
 };
 
 // Key (within a 32-key block) whose K row the lane feeding MFMA row `slot`
@@ -137,7 +139,9 @@ SEGKV_HD int k_swz(int row) { return row & (D / 8 - 1); }  // S^T reads: 16 rows
 // V(i) into the stages nobody reads any more; they land before the barrier
 // that ends slot 2i+1, ahead of the MFMA step of tile i+1. The V^T operand of
 // a 16-key page is one 16-byte read per lane: 8 consecutive keys of one d.
-template <int D>
+// kMask: every tile takes its visibility from the explicit mask (one byte per
+// kv head, query row and key) instead of the head-class rule.
+template <int D, bool kMask>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   constexpr int KS = D / 16;                 // MFMA k-steps over the head dim
@@ -184,6 +188,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
   const int lo_row = is_local ? local_lo(pos, mt.bq, mt.W) : 0;
   const int pos_min = mt.pos0, pos_max = mt.pos0 + mt.n_pos - 1;
   const int lo_max = is_local ? local_lo(pos_max, mt.bq, mt.W) : 0;
+  const uint8_t* mrow = kMask ? a.mask + ((size_t)mt.h * a.mask_rows + qrow) * a.mask_L + 8 * lg : nullptr;
 
   // the item's page table -> LDS (entries past the m-tile's end, or with an
   // invalid page id, become pid -1 / pos INT_MAX)
@@ -412,7 +417,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
     const int kmax = imax(imax(p0 == INT_MAX ? 0 : p0, p1 == INT_MAX ? 0 : p1),
                           imax(p2 == INT_MAX ? 0 : p2, p3 == INT_MAX ? 0 : p3)) + kPage - 1;
     const bool full = all_valid && kmax <= pos_min && (!is_local || kmin >= lo_max);
-    if (!full) {  // only tiles that straddle a window edge
+    if (kMask || !full) {  // the class rule masks only tiles that straddle a window edge
+      uint64_t mb[4] = {0, 0, 0, 0};  // mask mode: bytes of keys ps + 8 lg .. + 7 of each page
+      if (kMask) {
+        if (p0 != INT_MAX) mb[0] = *reinterpret_cast<const uint64_t*>(mrow + p0);
+        if (p1 != INT_MAX) mb[1] = *reinterpret_cast<const uint64_t*>(mrow + p1);
+        if (p2 != INT_MAX) mb[2] = *reinterpret_cast<const uint64_t*>(mrow + p2);
+        if (p3 != INT_MAX) mb[3] = *reinterpret_cast<const uint64_t*>(mrow + p3);
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -420,7 +432,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
           const int pp = 2 * kb + (e >> 3);
           const int ps = pp == 0 ? p0 : pp == 1 ? p1 : pp == 2 ? p2 : p3;
           const int j = ps + 8 * lg + (e & 7);
-          const bool vis = ps != INT_MAX && j <= pos && j >= lo_row;
+          const bool vis = kMask ? ((mb[pp] >> (8 * (e & 7))) & 0xffu) != 0
+                                 : ps != INT_MAX && j <= pos && j >= lo_row;
           sc[kb][e] = vis ? sc[kb][e] : -INFINITY;
         }
     }
@@ -639,12 +652,11 @@ const uint16_t* zero_page_address() {
 
 using namespace segkv;
 
-extern "C" int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_meta* meta_host, const void* q,
-                                         const void* k_pool, const void* v_pool, int64_t pool_pages,
-                                         const int32_t* page_ids_dev, const int32_t* page_pos_dev,
-                                         const void* plan_dev, size_t plan_bytes, float softmax_scale, void* out,
-                                         float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  clear_error();
+namespace {
+int32_t attn_prefill(const segkv_dims* dims, const segkv_meta* meta_host, const void* q, const void* k_pool,
+                     const void* v_pool, int64_t pool_pages, const int32_t* page_ids_dev, const int32_t* page_pos_dev,
+                     const void* plan_dev, size_t plan_bytes, float softmax_scale, const uint8_t* mask,
+                     int64_t mask_L, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   HostPlan hp;
   int32_t st = compute_host_plan(dims, meta_host, &hp);
   if (st != SEGKV_OK) return st;
@@ -680,16 +692,58 @@ extern "C" int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_met
   a.scale_log2 = softmax_scale * kLog2e;
   a.Hq = dims->num_q_heads;
   a.G = dims->num_q_heads / dims->num_kv_heads;
+  a.mask = mask;
+  a.mask_rows = hp.total_q_rows;
+  a.mask_L = mask_L;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dims->head_dim == 128) {
-    attn_main_kernel<128><<<hp.n_items, kAttnThreads, 0, s>>>(a);
+    if (mask)
+      attn_main_kernel<128, true><<<hp.n_items, kAttnThreads, 0, s>>>(a);
+    else
+      attn_main_kernel<128, false><<<hp.n_items, kAttnThreads, 0, s>>>(a);
     SEGKV_LAUNCH_CHECK();
     if (hp.n_split > 0) attn_combine_kernel<128><<<dim3(hp.n_split, kMRows * 32 / kCombineThreads), kCombineThreads, 0, s>>>(a);
   } else {
-    attn_main_kernel<64><<<hp.n_items, kAttnThreads, 0, s>>>(a);
+    if (mask)
+      attn_main_kernel<64, true><<<hp.n_items, kAttnThreads, 0, s>>>(a);
+    else
+      attn_main_kernel<64, false><<<hp.n_items, kAttnThreads, 0, s>>>(a);
     SEGKV_LAUNCH_CHECK();
     if (hp.n_split > 0) attn_combine_kernel<64><<<dim3(hp.n_split, kMRows * 16 / kCombineThreads), kCombineThreads, 0, s>>>(a);
   }
   SEGKV_LAUNCH_CHECK();
   return SEGKV_OK;
+}
+}  // namespace
+
+extern "C" int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_meta* meta_host, const void* q,
+                                         const void* k_pool, const void* v_pool, int64_t pool_pages,
+                                         const int32_t* page_ids_dev, const int32_t* page_pos_dev,
+                                         const void* plan_dev, size_t plan_bytes, float softmax_scale, void* out,
+                                         float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  return attn_prefill(dims, meta_host, q, k_pool, v_pool, pool_pages, page_ids_dev, page_pos_dev, plan_dev,
+                      plan_bytes, softmax_scale, nullptr, 0, out, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" int32_t segpaged_attn_prefill_masked(const segkv_dims* dims, const segkv_meta* meta_host, const void* q,
+                                                const void* k_pool, const void* v_pool, int64_t pool_pages,
+                                                const int32_t* page_ids_dev, const int32_t* page_pos_dev,
+                                                const void* plan_dev, size_t plan_bytes, float softmax_scale,
+                                                const uint8_t* mask, int64_t mask_L, void* out, float* lse,
+                                                void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  const int32_t st = validate_layout(dims, meta_host);
+  if (st != SEGKV_OK) return st;
+  int64_t need = 0;
+  for (int r = 0; r < dims->num_requests; ++r) {
+    const int sq = meta_host->seg_indptr[r + 1] - 1;
+    need = std::max<int64_t>(need, ((int64_t)meta_host->seg_start[sq] + meta_host->seg_len[sq] + kPage - 1) / kPage * kPage);
+  }
+  if (!mask) return fail(SEGKV_ERR_INVALID_ARG, "mask is NULL");
+  if (!aligned16(mask)) return fail(SEGKV_ERR_ALIGNMENT, "mask must be 16-byte aligned");
+  if (mask_L % kPage != 0 || mask_L < need)
+    return fail(SEGKV_ERR_INVALID_ARG, "mask_L must be a multiple of 16 covering every request's last page");
+  return attn_prefill(dims, meta_host, q, k_pool, v_pool, pool_pages, page_ids_dev, page_pos_dev, plan_dev,
+                      plan_bytes, softmax_scale, mask, mask_L, out, lse, workspace, workspace_bytes, stream);
 }

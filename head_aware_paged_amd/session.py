@@ -19,7 +19,8 @@ import torch
 
 from . import (HostMeta, dims, rope_relocate, segkv_build_pages, segkv_decode_workspace_size,
                segkv_out_proj_residual, segkv_plan_sizes, segkv_qkv_rope_append, segkv_qkv_workspace_size,
-               segkv_visible_spans, segpaged_attn_decode, segpaged_attn_prefill, sparse_ffn_swiglu,
+               segkv_visible_spans, segpaged_attn_decode, segpaged_attn_prefill, segpaged_attn_prefill_masked,
+               sparse_ffn_swiglu,
                sparse_ffn_workspace_size, token_importance_topk)
 
 
@@ -84,6 +85,18 @@ class SegPagedLayer:
             lse = torch.empty(T, Hq, dtype=torch.float32, device=self.device)
         segpaged_attn_prefill(self.dims, self.meta, q, k_pool, v_pool, self.page_ids, self.page_pos, self.plan,
                               self.scale, out, lse, self.workspace, stream=stream)
+        return out, lse
+
+    def attention_masked(self, q, k_pool, v_pool, mask, out=None, lse=None, want_lse=True, stream=None):
+        """Attention with visibility from an explicit mask [Hkv][T_q][L] (uint8) over this
+        layer's page tables (all-global tables: the dense layout)."""
+        T, Hq, D = int(self.cu_q_host[-1]), self.dims.num_q_heads, self.dims.head_dim
+        if out is None:
+            out = torch.empty(T, Hq, D, dtype=torch.bfloat16, device=self.device)
+        if lse is None and want_lse:
+            lse = torch.empty(T, Hq, dtype=torch.float32, device=self.device)
+        segpaged_attn_prefill_masked(self.dims, self.meta, q, k_pool, v_pool, self.page_ids, self.page_pos,
+                                     self.plan, self.scale, mask, out, lse, self.workspace, stream=stream)
         return out, lse
 
     def decode(self, q_new, k_new, v_new, k_pool, v_pool, out=None, lse=None, want_lse=True, stream=None):

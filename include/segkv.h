@@ -187,6 +187,27 @@ int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_meta* meta_hos
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same attention with an explicit mask in place of the class rule: the
+ * tuned form of the masked-dense comparator (paooo.com "RedKnot的技术原理":
+ * the fused kernel replaces a dense layout plus mask). Every key tile of
+ * every m-tile reads mask[h][t][j] (t = batch query row, j = key position in
+ * the row's request; nonzero = visible) instead of applying the head class.
+ * Built with every kv head GLOBAL, the page tables hold every page up to
+ * each request's end, which is the dense layout; keys after an m-tile's last
+ * row position are still not computed, so the mask can only remove keys.
+ * Every row's mask must keep at least one key (else its output is undefined).
+ * Arguments as segpaged_attn_prefill, plus mask: device bytes
+ * [Hkv][T_q][mask_L], 16-byte aligned; mask_L a multiple of 16 covering the
+ * last page of every request (else SEGKV_ERR_INVALID_ARG).
+ */
+int32_t segpaged_attn_prefill_masked(const segkv_dims* dims, const segkv_meta* meta_host,
+                                     const void* q, const void* k_pool, const void* v_pool, int64_t pool_pages,
+                                     const int32_t* page_ids_dev, const int32_t* page_pos_dev,
+                                     const void* plan_dev, size_t plan_bytes, float softmax_scale,
+                                     const uint8_t* mask, int64_t mask_L, void* out, float* lse,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decode-phase attention: one new query row per request, the next step of the
  * same requests (arXiv abstract: long-context generation; paooo.com
  * "如何使用RedKnot": EXECUTE over the visible state chosen per head).
@@ -307,6 +328,26 @@ int32_t segkv_qkv_rope_append(const segkv_dims* dims, const segkv_meta* meta_hos
  */
 int32_t segkv_out_proj_residual(const void* attn, int32_t n_rows, int32_t in_features, const void* w_o,
                                 void* hidden, int32_t hidden_size, void* stream);
+
+/*
+ * Masked-dense attention, the comparator of the paged head-aware layout
+ * (paooo.com "RedKnot的技术原理", "RedKnot的核心优势": the fused varlen kernel
+ * replaces a dense layout plus an attention mask, quoted as several times
+ * slower). One request: for query row t and query head g (kv head
+ * h = g / (Hq/Hkv)),
+ *   O[t][g] = sum_j softmax_j( scale * q[t][g] . k[h][j] | mask[h][t][j] != 0 ) v[h][j]
+ * over every key j < L; every score is computed, the mask only removes keys
+ * from the softmax. A row whose mask is all zero gets O = 0, LSE = -inf.
+ * q: [T][Hq][D] bf16; k: [Hkv][L][D] bf16; v_t: [Hkv][D][L] bf16 (V stored
+ * d-major, element (j, d) at d * L + j); mask: [Hkv][T][L] bytes;
+ * out: [T][Hq][D] bf16; lse: [T][Hq] fp32 natural log (nullable).
+ * workspace: segkv_masked_dense_workspace_size bytes (split-KV partials).
+ * Limits: D in {64, 128}; L a multiple of 64 (pad with masked keys).
+ */
+int32_t segkv_masked_dense_workspace_size(int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t L, size_t* bytes);
+int32_t masked_dense_attn(const void* q, const void* k, const void* v_t, const uint8_t* mask, int32_t T, int32_t Hq,
+                          int32_t Hkv, int32_t D, int32_t L, float softmax_scale, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

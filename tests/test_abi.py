@@ -19,7 +19,7 @@ def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(segkv_\w+|rope_relocate|segpaged_attn_\w+|token_importance_topk|"
-                                 r"sparse_ffn_\w+)\s*\(", src)))
+                                 r"sparse_ffn_\w+|masked_dense_attn)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
