@@ -18,7 +18,7 @@ Parity status per function:
   decode attention (brute force + vectorised, and against the prefill
   attention of a one-token-longer query segment), importance, top-k, sparse
   FFN, the layer glue (projection + RoPE + append, output projection),
-  masked-dense attention: pinned by ``tests/test_oracle_*.py``.
+  masked-dense attention, the elastic layer stack: pinned by ``tests/test_oracle_*.py``.
   Agreement with RedKnot's own implementation (its RoPE pairing, window
   inclusivity, dense-vs-global semantics) cannot be pinned: the pages print
   no worked example. That end-to-end numerical match is "parity unpinned".
@@ -33,4 +33,5 @@ from .decode import decode, decode_brute  # noqa: F401
 from .importance import importance, topk_select  # noqa: F401
 from .ffn import sparse_ffn  # noqa: F401
 from .dense import dense_layout, masked_dense  # noqa: F401
+from .stack import shallow_layout, stack  # noqa: F401
 from .layer import row_positions, qkv_rope, append_query_kv, out_proj_residual, layer  # noqa: F401
