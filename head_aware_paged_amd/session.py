@@ -19,7 +19,7 @@ import torch
 
 from . import (HostMeta, dims, rope_relocate, segkv_build_pages, segkv_decode_workspace_size,
                segkv_out_proj_residual, segkv_plan_sizes, segkv_qkv_rope_append, segkv_qkv_workspace_size,
-               segkv_visible_spans, segpaged_attn_decode, segpaged_attn_prefill, segpaged_attn_prefill_masked,
+               segkv_topk_select, segkv_visible_spans, segpaged_attn_decode, segpaged_attn_prefill, segpaged_attn_prefill_masked,
                sparse_ffn_swiglu,
                sparse_ffn_workspace_size, token_importance_topk)
 
@@ -158,3 +158,58 @@ class SparseFFN:
     def __call__(self, hidden, idx, k: int, stream=None):
         sparse_ffn_swiglu(hidden, idx, k, self.w_gate, self.w_up, self.w_down, self.workspace, stream=stream)
         return hidden
+
+
+class ElasticStack:
+    """A stack of attention + FFN layers over one segment layout (one request)
+    under the layer-wise elastic policy (RedKnot README "About": Elastic
+    Sparsity): layers below ``n_shallow`` treat every kv head as LOCAL(window)
+    and run the dense FFN on every query row; deeper layers use the layout's
+    class map and run the FFN on the ``k`` query rows of highest attention
+    importance over the last ``n_last`` rows. Each layer brings its weights
+    and its own working pools: dict(w_qkv, w_o, w_gate, w_up, w_down, k_pool,
+    v_pool) of device tensors; every layer's pools use the one page mapping
+    (seg_page_indptr, seg_pages)."""
+
+    def __init__(self, num_q_heads: int, num_kv_heads: int, head_dim: int, seg_indptr, seg_start, seg_len,
+                 head_class, window, retr_seg, seg_page_indptr, seg_pages, layers, n_shallow: int,
+                 shallow_window: int, k: int, n_last: int, rope_theta: float, device: str = "cuda"):
+        if len(seg_indptr) != 2:
+            raise ValueError("the elastic stack runs one request")
+        hc = np.asarray(head_class)
+        self.deep = SegPagedLayer(num_q_heads, num_kv_heads, head_dim, seg_indptr, seg_start, seg_len, hc, window,
+                                  retr_seg, device=device)
+        self.shallow = SegPagedLayer(num_q_heads, num_kv_heads, head_dim, seg_indptr, seg_start, seg_len,
+                                     np.full_like(hc, 1), np.full(len(hc), shallow_window, np.int32),
+                                     np.full(len(hc) * 2, -1, np.int32), device=device)
+        self.spi, self.spg = seg_page_indptr, seg_pages
+        for lay in (self.deep, self.shallow):
+            lay.build_pages(seg_page_indptr, seg_pages)
+        self.layers, self.n_shallow, self.k, self.n_last, self.theta = layers, n_shallow, k, n_last, rope_theta
+        self.T = int(self.deep.cu_q_host[-1])
+        self.bq = int(np.asarray(seg_start)[-1])
+        self.all_rows = torch.arange(self.T, dtype=torch.int32, device=device)
+        self.idx = [torch.empty(max(1, k), dtype=torch.int32, device=device) for _ in layers]
+        self.imp = torch.empty(int(self.deep.sizes["total_keys"]), dtype=torch.float32, device=device)
+        inter = layers[0]["w_gate"].shape[0]
+        self.ffn_ws = torch.empty(max(16, sparse_ffn_workspace_size(self.T, inter)), dtype=torch.uint8,
+                                  device=device)
+
+    def forward(self, hidden, stream=None):
+        """hidden: [T_q][hidden] bf16, updated in place. Returns the rows each layer's FFN took."""
+        chosen = []
+        for li, L in enumerate(self.layers):
+            lay = self.shallow if li < self.n_shallow else self.deep
+            q = lay.qkv_rope_append(hidden, L["w_qkv"], self.theta, self.spi, self.spg, L["k_pool"], L["v_pool"],
+                                    stream=stream)
+            out, lse = lay.attention(q, L["k_pool"], L["v_pool"], stream=stream)
+            lay.out_proj_residual(out, L["w_o"], hidden, stream=stream)
+            if li < self.n_shallow:
+                idx, k = self.all_rows, self.T
+            else:
+                lay.importance_topk(q, L["k_pool"], lse, self.n_last, None, importance=self.imp, stream=stream)
+                idx, k = self.idx[li], self.k
+                segkv_topk_select(self.imp[self.bq:self.bq + self.T], self.T, k, idx, stream=stream)
+            sparse_ffn_swiglu(hidden, idx, k, L["w_gate"], L["w_up"], L["w_down"], self.ffn_ws, stream=stream)
+            chosen.append(idx)
+        return chosen

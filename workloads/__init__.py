@@ -81,8 +81,11 @@ def layer_inputs(w, hidden_size: int, seed: int = 0):
 def stack_inputs(w, n_layers: int, hidden_size: int, inter: int, seed: int = 0):
     """Per-layer weights of a synthetic stack over w's layout: list of dicts of
     bf16 bit patterns (w_qkv, w_o as in ``layer_inputs``; w_gate, w_up
-    ~ N(0, 1/hidden_size), w_down ~ N(0, 1/inter)), plus the query rows'
-    residual stream [T_q, hidden_size] ~ N(0, 1). Input recipe only."""
+    ~ N(0, 1/hidden_size), w_down ~ N(0, 0.04/inter)), plus the query rows'
+    residual stream [T_q, hidden_size] ~ N(0, 1). Input recipe only. The
+    small down projection keeps the residual stream of order one through the
+    layers: with no normalisation layer, SwiGLU grows with the square of
+    its input, and unit-scale weights let the stream grow layer after layer."""
     rng = np.random.Generator(np.random.PCG64(30_000 + seed))
     Hq, Hkv, D, T = w.num_q_heads, w.num_kv_heads, w.head_dim, w.total_q_rows
     hidden = _normal_bf16(rng, (T, hidden_size))
@@ -93,7 +96,7 @@ def stack_inputs(w, n_layers: int, hidden_size: int, inter: int, seed: int = 0):
             w_o=_normal_bf16(rng, (hidden_size, Hq * D), std=(Hq * D) ** -0.5),
             w_gate=_normal_bf16(rng, (inter, hidden_size), std=hidden_size ** -0.5),
             w_up=_normal_bf16(rng, (inter, hidden_size), std=hidden_size ** -0.5),
-            w_down=_normal_bf16(rng, (hidden_size, inter), std=inter ** -0.5)))
+            w_down=_normal_bf16(rng, (hidden_size, inter), std=0.2 * inter ** -0.5)))
     return hidden, layers
 
 @dataclasses.dataclass
