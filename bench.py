@@ -443,6 +443,47 @@ def main():
         log(f"masked dense (tuned kernel, mask mode) {t_gm * 1e3:.1f} us, {t_gm / t_attn:.2f}x the SegPaged attention")
         del dmask, ggraph, glayer
 
+        # layer-wise elastic policy: 4 layers of the 32K layout (2 shallow: all-local heads + dense FFN;
+        # 2 deep: the class map + FFN on the top 25 % query rows), against 4 uniform layers (class map + dense FFN)
+        from head_aware_paged_amd.session import ElasticStack
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        inter = 14336
+
+        def rnd(*shape, std):
+            return (torch.randn(*shape, generator=gen, device=dev) * std).to(torch.bfloat16)
+        slayers = []
+        for _ in range(4):
+            slayers.append(dict(w_qkv=rnd((Hq + 2 * Hkv) * D, hs, std=hs ** -0.5), w_o=rnd(hs, Hq * D, std=(Hq * D) ** -0.5),
+                                w_gate=rnd(inter, hs, std=hs ** -0.5), w_up=rnd(inter, hs, std=hs ** -0.5),
+                                w_down=rnd(hs, inter, std=0.2 * inter ** -0.5), k_pool=k_work, v_pool=v_work))
+        shid0 = rnd(T, hs, std=1.0)
+        shid = shid0.clone()
+        stack_args = (Hq, Hkv, D, w.seg_indptr, w.seg_start, w.seg_len, w.head_class, w.window, w.retr_seg,
+                      seg_pi, seg_pg, slayers)
+        res = {}
+        for name, n_sh, kk in (("elastic", 2, T // 4), ("uniform", 0, T)):
+            st = ElasticStack(*stack_args, n_shallow=n_sh, shallow_window=1024, k=kk, n_last=64,
+                              rope_theta=w.rope_theta)
+
+            def fwd(st=st):
+                shid.copy_(shid0)
+                st.forward(shid)
+            fwd()
+            torch.cuda.synchronize()
+            sg = capture(fwd)
+            res[name] = time_graph(sg, 5)
+            del sg, st
+        result["elastic_stack_32k"] = {
+            "layers": 4, "hidden": hs, "inter": inter, "elastic_us": res["elastic"] * 1e3,
+            "uniform_us": res["uniform"] * 1e3, "speedup": res["uniform"] / res["elastic"],
+            "elastic": "layers 0-1 all-local(1024) + dense FFN; layers 2-3 class map + FFN on the top 128 of 512 rows",
+            "uniform": "every layer the class map + dense FFN",
+            "note": "random-init weights; the layers share one set of pools (timing only)"}
+        log(f"elastic stack {res['elastic'] * 1e3:.0f} us vs uniform {res['uniform'] * 1e3:.0f} us "
+            f"({res['uniform'] / res['elastic']:.2f}x)")
+        del slayers, shid, shid0
+
         # sparse SwiGLU FFN of the 8K selection workload (k = 2048 rows, 4096 -> 14336)
         log("generating sparse_ffn_8k FFN inputs")
         w5 = workloads.sparse_ffn_8k()

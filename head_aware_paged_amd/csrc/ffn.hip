@@ -26,6 +26,10 @@ constexpr int kRowsA = 128, kRowsB = 128;
 
 enum { kModeSwiglu = 0, kModeResidual = 1 };
 
+// 128-row token tiles leave CUs idle when a launch has fewer than two
+// work-groups per CU (256 CUs); 64-row tiles double the count.
+inline bool small_grid(int n_tiles, int rows) { return (int64_t)n_tiles * cdiv(rows, kRowsB) < 512; }
+
 struct FfnArgs {
   const uint16_t* a0;   // weights: gate (SwiGLU) or down (residual)
   const uint16_t* a1;   // up weights (SwiGLU only)
@@ -372,7 +376,10 @@ extern "C" int32_t sparse_ffn_swiglu(void* hidden, int32_t n_rows, int32_t hidde
   g1.K = hidden_size;
   g1.out_ld = inter;
   g1.n_rows = n_rows;
-  ffn_gemm_kernel<kModeSwiglu, 2><<<dim3(inter / 64, cdiv(k, kRowsB)), kFfnThreads, 0, s>>>(g1);
+  if (small_grid(inter / 64, k))
+    ffn_gemm_kernel<kModeSwiglu, 1><<<dim3(inter / 64, cdiv(k, 64)), kFfnThreads, 0, s>>>(g1);
+  else
+    ffn_gemm_kernel<kModeSwiglu, 2><<<dim3(inter / 64, cdiv(k, kRowsB)), kFfnThreads, 0, s>>>(g1);
   SEGKV_LAUNCH_CHECK();
   FfnArgs g2;
   g2.a0 = static_cast<const uint16_t*>(w_down);
@@ -384,16 +391,15 @@ extern "C" int32_t sparse_ffn_swiglu(void* hidden, int32_t n_rows, int32_t hidde
   g2.K = inter;
   g2.out_ld = hidden_size;
   g2.n_rows = n_rows;
-  ffn_gemm_kernel<kModeResidual, 2><<<dim3(hidden_size / kRowsA, cdiv(k, kRowsB)), kFfnThreads, 0, s>>>(g2);
+  if (small_grid(hidden_size / kRowsA, k))
+    ffn_gemm_kernel<kModeResidual, 1><<<dim3(hidden_size / kRowsA, cdiv(k, 64)), kFfnThreads, 0, s>>>(g2);
+  else
+    ffn_gemm_kernel<kModeResidual, 2><<<dim3(hidden_size / kRowsA, cdiv(k, kRowsB)), kFfnThreads, 0, s>>>(g2);
   SEGKV_LAUNCH_CHECK();
   return SEGKV_OK;
 }
 
 namespace {
-// 128-row token tiles leave CUs idle when a launch has fewer than two
-// work-groups per CU (256 CUs); 64-row tiles double the count.
-bool small_grid(int n_tiles, int rows) { return (int64_t)n_tiles * cdiv(rows, kRowsB) < 512; }
-
 size_t qkv_ws_bytes(int64_t T, int Hkv, int D) {
   const size_t cs = ((size_t)T * (D / 2) * sizeof(float2) + 255) & ~(size_t)255;
   return cs + (size_t)T * Hkv * sizeof(int32_t);
