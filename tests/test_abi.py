@@ -150,3 +150,53 @@ def test_importance_validation():
     assert lib.token_importance_topk(*args(n_last=0)) == -1
     assert lib.token_importance_topk(*args(n_last=4096)) == -2
     assert lib.token_importance_topk(*args(plan_bytes=8)) == -5
+
+
+def test_glue_decode_comparator_validation():
+    """Host-side checks of the layer glue, decode and comparator entry points (nothing launched)."""
+    lib = hk.load()
+    d, m = _layout()
+    ms = m.struct()
+    dm = hk.Meta(16, 16, 16, 16, 16, 16)
+    n = ctypes.c_size_t(0)
+    assert lib.segkv_qkv_workspace_size(ctypes.byref(d), ctypes.byref(ms), ctypes.byref(n)) == 0 and n.value > 0
+    ws = n.value
+
+    def qkv(hidden_size=256, theta=1e4, ws_bytes=ws, hidden=16, pool_pages=10):
+        return lib.segkv_qkv_rope_append(ctypes.byref(d), ctypes.byref(ms), ctypes.byref(dm), 16, 16, 16,
+                                         pool_pages, hidden, hidden_size, 16, theta, 16, 16, 16, 16, ws_bytes, None)
+    assert qkv(hidden_size=100) == -2          # not a multiple of 64
+    assert qkv(theta=0.0) == -1
+    assert qkv(ws_bytes=ws - 1) == -5
+    assert qkv(hidden=8) == -4                 # misaligned
+    assert qkv(hidden=None) == -1
+    assert qkv(pool_pages=0) == -1
+    # output projection
+    assert lib.segkv_out_proj_residual(16, 4, 100, 16, 16, 128, None) == -2
+    assert lib.segkv_out_proj_residual(16, 4, 64, 16, 16, 100, None) == -2
+    assert lib.segkv_out_proj_residual(16, 0, 64, 16, 16, 128, None) == 0   # no rows: no-op
+    assert lib.segkv_out_proj_residual(8, 4, 64, 16, 16, 128, None) == -4
+    # decode: workspace size and a group size above 16
+    assert lib.segkv_decode_workspace_size(ctypes.byref(d), ctypes.byref(ms), ctypes.byref(n)) == 0
+    big = hk.dims(1, 68, 4, 64, 16, 4)
+    assert lib.segkv_decode_workspace_size(ctypes.byref(big), ctypes.byref(ms), ctypes.byref(n)) != 0
+    # standalone masked dense
+    assert lib.segkv_masked_dense_workspace_size(32, 8, 4, 64, 100, ctypes.byref(n)) == -2   # L % 64
+    assert lib.segkv_masked_dense_workspace_size(32, 8, 3, 64, 128, ctypes.byref(n)) == -1   # Hq % Hkv
+    assert lib.segkv_masked_dense_workspace_size(32, 8, 4, 80, 128, ctypes.byref(n)) == -2   # head_dim
+    assert lib.segkv_masked_dense_workspace_size(32, 8, 4, 64, 128, ctypes.byref(n)) == 0
+    dws = n.value
+    assert lib.masked_dense_attn(16, 16, 16, 16, 32, 8, 4, 64, 128, ctypes.c_float(0.125), 16, None, 16,
+                                 dws - 1, None) == -5
+    assert lib.masked_dense_attn(16, 16, 16, 8, 32, 8, 4, 64, 128, ctypes.c_float(0.125), 16, None, 16,
+                                 dws, None) == -4
+    assert lib.masked_dense_attn(16, 16, 16, 16, 32, 8, 4, 64, 128, ctypes.c_float(-1.0), 16, None, 16,
+                                 dws, None) == -1
+    # masked prefill: the mask must cover every request's last page
+    s = hk.segkv_plan_sizes(d, m)
+    margs = lambda mask, mask_L: [ctypes.byref(d), ctypes.byref(ms), 16, 16, 16, 10, 16, 16, 16, s["plan_bytes"],
+                                  ctypes.c_float(0.125), mask, mask_L, 16, None, 16, s["attn_workspace_bytes"], None]
+    assert lib.segpaged_attn_prefill_masked(*margs(None, 256)) == -1
+    assert lib.segpaged_attn_prefill_masked(*margs(16, 200)) == -1     # not a multiple of 16
+    assert lib.segpaged_attn_prefill_masked(*margs(16, 16)) == -1      # too short
+    assert lib.segpaged_attn_prefill_masked(*margs(8, 256)) == -4      # misaligned mask
