@@ -206,6 +206,7 @@ int32_t dense_check(int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t L) {
   if (D != 64 && D != 128) return fail(SEGKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (L % kDenKeys != 0) return fail(SEGKV_ERR_UNSUPPORTED, "L must be a multiple of 64 (pad with masked keys)");
   if ((int64_t)Hkv * T * L > (int64_t)1 << 40) return fail(SEGKV_ERR_UNSUPPORTED, "mask too large");
+  if ((int64_t)T * Hq > INT32_MAX) return fail(SEGKV_ERR_UNSUPPORTED, "T * Hq must fit in 31 bits");
   return SEGKV_OK;
 }
 
