@@ -484,6 +484,32 @@ def main():
             f"({res['uniform'] / res['elastic']:.2f}x)")
         del slayers, shid, shid0
 
+        # the attention on the two other full-size layouts: the 4-request varlen batch and the 64K layer
+        # (structure from the workload generators; pools and Q drawn on the device, N(0, 1) bf16)
+        from head_aware_paged_amd.session import SegPagedLayer
+        for wname, make in (("qwen3_32b_varlen", workloads.qwen_varlen), ("long_64k", workloads.long_64k)):
+            wx = make(with_data=False)
+            xl = SegPagedLayer(wx.num_q_heads, wx.num_kv_heads, wx.head_dim, wx.seg_indptr, wx.seg_start, wx.seg_len,
+                               wx.head_class, wx.window, wx.retr_seg, page_size=16, device=dev)
+            xl.build_pages(i32(wx.seg_page_indptr), i32(wx.seg_pages))
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(11)
+            Dx, np_ = wx.head_dim, wx.k_work.shape[0]
+            qx = torch.randn(wx.total_q_rows, wx.num_q_heads, Dx, generator=gen, device=dev).to(torch.bfloat16)
+            kx = torch.randn(np_, 16, Dx, generator=gen, device=dev).to(torch.bfloat16)
+            vx = torch.randn(np_, Dx, 16, generator=gen, device=dev).to(torch.bfloat16)
+            ox = torch.empty_like(qx)
+            lx = torch.empty(wx.total_q_rows, wx.num_q_heads, dtype=torch.float32, device=dev)
+            xg = capture(repeat(lambda: xl.attention(qx, kx, vx, out=ox, lse=lx)))
+            tx = time_graph(xg, 5) / per_graph
+            px = int(visible_pairs_per_row(wx).sum())
+            fx = 4.0 * Dx * px
+            result[f"attention_{wname}"] = {
+                "us": tx * 1e3, "visible_pairs": px, "gflop": fx / 1e9, "tflops": fx / (tx * 1e-3) / 1e12,
+                "pct_bf16_peak": 100.0 * fx / (tx * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+            log(f"attention {wname}: {tx * 1e3:.1f} us, {fx / (tx * 1e-3) / 1e12:.0f} TFLOP/s")
+            del xl, qx, kx, vx, ox, lx, xg
+
         # sparse SwiGLU FFN of the 8K selection workload (k = 2048 rows, 4096 -> 14336)
         log("generating sparse_ffn_8k FFN inputs")
         w5 = workloads.sparse_ffn_8k()
