@@ -11,7 +11,9 @@
 // A work-group takes a batch of 1 (D = 128) or 2 (D = 64) moves, so that a
 // layer's few thousand moves spread over many work-groups per CU; it keeps all
 // 16-byte loads of the batch in flight and computes the batch's cos/sin table
-// (fp64 sincos, rounded to fp32, in LDS) while they fly.
+// (angle reduced in fp64, cos/sin in fp32, in LDS) while they fly.
+#include <cmath>
+
 #include "common.h"
 
 namespace segkv {
@@ -25,7 +27,7 @@ template <int D>
 __global__ __launch_bounds__(kRelocThreads) void relocate_kernel(
     const uint16_t* __restrict__ k_src, uint16_t* __restrict__ k_dst, const uint16_t* __restrict__ v_src,
     uint16_t* __restrict__ v_dst, int64_t src_pages, int64_t dst_pages, const int32_t* __restrict__ src_page,
-    const int32_t* __restrict__ dst_page, const int32_t* __restrict__ delta, int n_moves, double theta) {
+    const int32_t* __restrict__ dst_page, const int32_t* __restrict__ delta, int n_moves, double log2_theta) {
   constexpr int kMovesPerBatch = moves_per_batch<D>();
   constexpr int kHalf = D / 2;
   constexpr int kChunksPerHalf = kHalf / 8;          // 16-byte chunks in one half row
@@ -78,14 +80,19 @@ __global__ __launch_bounds__(kRelocThreads) void relocate_kernel(
       if (s_ok[b]) vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_src + (size_t)s_src[b] * kPage * D) + w);
     }
   }
-  if (tid < kHalf) inv_freq[tid] = pow(theta, -2.0 * (double)tid / (double)D);
+  if (tid < kHalf) inv_freq[tid] = exp2(-2.0 * (double)tid / (double)D * log2_theta);
   __syncthreads();
   for (int e = tid; e < kMovesPerBatch * kHalf; e += kRelocThreads) {
     const int b = e / kHalf, j = e % kHalf;
-    double sn = 0.0, cn = 1.0;
-    if (s_ok[b]) sincos((double)s_delta[b] * inv_freq[j], &sn, &cn);
-    cs[b][j][0] = (float)cn;
-    cs[b][j][1] = (float)sn;
+    float sn = 0.f, cn = 1.f;
+    if (s_ok[b]) {
+      // angle in fp64, reduced to [-pi, pi] in fp64 (2 pi in two parts), cos/sin in fp32
+      const double ang = (double)s_delta[b] * inv_freq[j];
+      const double n = rint(ang * 0.15915494309189535);
+      sincosf((float)fma(-n, 2.4492935982947064e-16, fma(-n, 6.283185307179586, ang)), &sn, &cn);
+    }
+    cs[b][j][0] = cn;
+    cs[b][j][1] = sn;
   }
 
   __syncthreads();
@@ -158,10 +165,10 @@ extern "C" int32_t rope_relocate(const void* k_src, void* k_dst, const void* v_s
   auto vd = static_cast<uint16_t*>(v_dst);
   if (head_dim == 128)
     relocate_kernel<128><<<grid, kRelocThreads, 0, s>>>(ks, kd, vs, vd, src_pool_pages, dst_pool_pages,
-                                                        src_page_dev, dst_page_dev, delta_dev, n_moves, rope_theta);
+                                                        src_page_dev, dst_page_dev, delta_dev, n_moves, std::log2(rope_theta));
   else
     relocate_kernel<64><<<grid, kRelocThreads, 0, s>>>(ks, kd, vs, vd, src_pool_pages, dst_pool_pages,
-                                                       src_page_dev, dst_page_dev, delta_dev, n_moves, rope_theta);
+                                                       src_page_dev, dst_page_dev, delta_dev, n_moves, std::log2(rope_theta));
   SEGKV_LAUNCH_CHECK();
   return SEGKV_OK;
 }

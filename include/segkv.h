@@ -151,7 +151,8 @@ int32_t segkv_visible_spans(const segkv_dims* dims, const segkv_meta* meta_host,
  * positions of K page src_page[m] of k_src, and (if v_src != NULL) V page
  * dst_page[m] of v_dst = copy of V page src_page[m] of v_src.
  * Rotation: rotate-half pairs (j, j + D/2), angle delta * theta^(-2j/D);
- * cos/sin from fp64, products in fp32, result rounded to bf16 (RNE).
+ * angle formed and reduced modulo 2 pi in fp64, cos/sin in fp32, products in
+ * fp32, result rounded to bf16 (RNE).
  * Pools: K [pages][page_size][head_dim] bf16 (token-major), V [pages][head_dim]
  * [page_size] bf16 (d-major); k_src/v_src with src_pool_pages pages and
  * k_dst/v_dst with dst_pool_pages pages. V pages are copied verbatim. Moves with a page id out of
