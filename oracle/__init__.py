@@ -25,9 +25,9 @@ Parity status per function:
 """
 from .bf16 import bf16_bits_to_f64, round_bf16, f64_to_bf16_bits, ulp_bf16  # noqa: F401
 from .rope import inv_freq, rope, relocate  # noqa: F401
-from .store import gather_kv, gather_cache_k  # noqa: F401
+from .store import gather_kv  # noqa: F401
 from .visibility import (visible_brute, visible_intervals, page_table, page_tables,  # noqa: F401
-                         visible_spans, move_list, visible_count, row_position)
+                         visible_spans, move_list, visible_count)
 from .attention import attention, attention_brute  # noqa: F401
 from .decode import decode, decode_brute  # noqa: F401
 from .importance import importance, topk_select  # noqa: F401

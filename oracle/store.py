@@ -29,9 +29,3 @@ def gather_kv(w, r, h, k_pool=None, v_pool=None):
         ks.append(_seg_tokens(k_pool, w.seg_page_indptr, w.seg_pages, s, h, Hkv, n))
         vs.append(_seg_tokens(v_pool, w.seg_page_indptr, w.seg_pages, s, h, Hkv, n))
     return bf16_bits_to_f64(np.concatenate(ks)), bf16_bits_to_f64(np.concatenate(vs))
-
-
-def gather_cache_k(w, s, h):
-    """Cached K of reused segment s, kv head h, at its original positions: fp64 [n_s, D]."""
-    return bf16_bits_to_f64(_seg_tokens(w.k_cache, w.cache_page_indptr, w.cache_pages, s, h,
-                                        w.num_kv_heads, int(w.seg_len[s])))

@@ -24,10 +24,6 @@ import numpy as np
 GLOBAL, LOCAL, RETRIEVAL, DENSE = 0, 1, 2, 3
 
 
-def row_position(w, r, t):
-    return int(w.seg_start[w.query_segment(r)]) + int(t)
-
-
 def _head(w, r, h):
     k = r * w.num_kv_heads + h
     return int(w.head_class[k]), int(w.window[k]), [int(x) for x in w.retr_seg[2 * k:2 * k + 2]]

@@ -129,3 +129,47 @@ def test_spans_and_moves():
     assert [tuple(x) for x in sp3[0, 0]] == [(0, 64), (96, 144), (208, 209)]
     # request 1 head 2: retrieval of both reused segments [0,16) and [16,32), query at 32 -> one span
     assert [tuple(x) for x in sp3[27, 2]] == [(0, 33), (-1, -1), (-1, -1)]
+
+
+def _moves_by_token_walk(w):
+    """Head-aware moves rebuilt from scratch by walking every visible token:
+    for each (r, h) in order, every key some query row sees (per-index
+    predicate) that lies in a reused segment names its page; that page's cache
+    copy moves to its working copy, shifted by the segment's delta. Pages are
+    listed once, in ascending position."""
+    P, Hkv = w.page_size, w.num_kv_heads
+    src, dst, delta = [], [], []
+    for r in range(w.num_requests):
+        sq = w.query_segment(r)
+        bq = int(w.seg_start[sq])
+        for h in range(Hkv):
+            keys = set()
+            for t in range(int(w.cu_q[r + 1] - w.cu_q[r])):
+                keys.update(oracle.visible_brute(w, r, h, bq + t))
+            seen = set()
+            for j in sorted(keys):
+                s = next(s for s in w.segments_of(r)
+                         if int(w.seg_start[s]) <= j < int(w.seg_start[s]) + int(w.seg_len[s]))
+                if s == sq or j // P in seen:
+                    continue
+                seen.add(j // P)
+                qp = (j - int(w.seg_start[s])) // P
+                src.append(int(w.cache_pages[w.cache_page_indptr[s * Hkv + h] + qp]))
+                dst.append(int(w.seg_pages[w.seg_page_indptr[s * Hkv + h] + qp]))
+                delta.append(int(w.seg_start[s]) - int(w.seg_orig_start[s]))
+    return src, dst, delta
+
+
+def test_move_list_token_walk():
+    # RedKnot README "About" (per-head page tables) and paooo.com "如何使用RedKnot"
+    # (SELECTVISIBLESTATE: only the KV a head can see is reused and relocated):
+    # every (cache page, working page, delta) triple is the one the token walk
+    # names, in the same order; the variants cover negative deltas (original
+    # starts past the new ones), retrieval heads, windows that cut a segment and
+    # two requests.
+    for w in _variants():
+        src, dst, delta = oracle.move_list(w)
+        s2, d2, dl2 = _moves_by_token_walk(w)
+        assert list(src) == s2 and list(dst) == d2 and list(delta) == dl2, w.name
+    w3 = next(v for v in _variants() if v.name == "tiny_retr")
+    assert min(oracle.move_list(w3)[2]) < 0
