@@ -6,9 +6,9 @@
 // RedKnot README "About": every head class has its own visible window over a
 // per-head page table.
 //
-// Work decomposition. A work-group (4 waves) owns one m-tile: the G query heads
-// of one kv head times 128/G consecutive query positions (128 rows), so every
-// K/V page staged in LDS serves all G heads of the group. The m-tile's visible
+// Work decomposition. A work-group (8 waves, two per SIMD) owns one m-tile: the
+// G query heads of one kv head times 256/G consecutive query positions (256
+// rows), so every K/V page staged in LDS serves all G heads of the group. The m-tile's visible
 // table entries are walked in tiles of 4 pages (64 keys); long ranges are split
 // into chunks whose partial (m, l, O) are merged by a second kernel. Items run
 // in an XCD-aware order: the m-tiles that read the same key chunk are launched
@@ -24,7 +24,6 @@
 // Visibility is a per-element predicate evaluated only on tiles that straddle
 // a window edge; other tiles take no mask work at all.
 #include <mutex>
-#include <type_traits>
 
 #include "common.h"
 
@@ -110,35 +109,33 @@ __device__ __forceinline__ float max_halves(float x) {
 #endif
 }
 
-// LDS of one work-group: two stages of K and V tiles, plus the item's page
-// table. K pages are token-major ([key][d]) with their 16-byte chunks
-// XOR-swizzled per row; V pages are d-major ([d][16 keys], as stored in the
-// pool) with the two 16-byte halves of a row swapped on every other group of
-// 8 rows. Both operand reads below are then free of bank conflicts and full
-// 16-byte reads. Every stage is its own __shared__ object and the loop is
-// unrolled by the stage index, so the compiler can tell that reads of one
-// stage do not alias the asynchronous copies into the other and does not wait
-// on those copies.
+// LDS of one work-group: three stages of K and three of V tiles, plus the
+// item's page table. K pages are token-major ([key][d]) with their 16-byte
+// chunks XOR-swizzled per row; V pages are d-major ([d][16 keys], as stored in
+// the pool) with the two 16-byte halves of a row swapped on every other group
+// of 8 rows. Both operand reads below are then free of bank conflicts and full
+// 16-byte reads.
 
 // (host+device so the device lambdas below may call them)
 template <int D>
 SEGKV_HD int k_swz(int row) { return row & (D / 8 - 1); }  // S^T reads: 16 rows, one chunk
 
 
-// Per item, key tiles i = 0 .. T-1 (T = t_hi - t_lo, T >= 1) in two LDS
-// stages: K(i) and V(i) live in stage i & 1. The work-group's 8 waves (32 rows
-// each) form two sets with one wave of each on every SIMD (the SIMD id comes
-// from the hardware), which run the same steps one slot apart:
-//   MFMA step of tile i:    S(i) = K(i) Q^T, then O += V(i-1)^T P(i-1)
-//   softmax step of tile i: mask, row max, P(i) = exp2(S(i) - m), l
-// Between two barriers (a slot), set 0 runs the MFMA step of tile s/2 while
-// set 1 runs the softmax step of tile s/2 - 1 (s even), or the softmax step of
-// tile (s-1)/2 while set 1 runs its MFMA step (s odd). Each SIMD's matrix core
-// then works for one of its two waves while the other does vector work. At the
-// start of slot 2i every wave issues its share of the copies of K(i+1) and
-// V(i) into the stages nobody reads any more; they land before the barrier
-// that ends slot 2i+1, ahead of the MFMA step of tile i+1. The V^T operand of
-// a 16-key page is one 16-byte read per lane: 8 consecutive keys of one d.
+// Per item, key tiles i = 0 .. T-1 (T = t_hi - t_lo, T >= 1). Each of the 8
+// waves owns 32 query rows. The two waves of every SIMD form two sets that
+// alternate between a matrix step and a softmax step, one barrier per slot:
+//   matrix step of tile i:   S(i) = K(i) Q^T, then O += V(i-1)^T P(i-1)
+//   softmax step of tile i:  mask, row max, P(i) = exp2(S(i) - m) in bf16, row sums
+// In slot 2i set 0 runs the matrix step of tile i while set 1 runs the
+// softmax step of tile i-1; in slot 2i+1 the other way round. So each SIMD's
+// matrix core works for one wave while the other issues vector work. K and V
+// tiles are copied straight into LDS (buffer loads with the LDS destination),
+// three stages each, tile j in stage j % 3; the copies of K(i+2) and V(i+1)
+// are issued in slots 2i / 2i+1 and have landed by slot 2i+4. Stages are
+// addressed at run time, so each set's loop body is a single copy of the code.
+// The V^T operand of a 16-key page is one 16-byte LDS read per lane: 8
+// consecutive keys of one d. A rescale of O found due by the softmax step of
+// tile i is applied before the PV product of tile i.
 // kMask: every tile takes its visibility from the explicit mask (one byte per
 // kv head, query row and key) instead of the head-class rule.
 template <int D, bool kMask>
@@ -147,19 +144,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
   constexpr int KS = D / 16;                 // MFMA k-steps over the head dim
   constexpr int DB = D / 32;                 // 32-wide d blocks of O^T
   constexpr int KCH = D / 8;                 // 16-byte chunks per K row
-  constexpr int RPK = 1024 / (2 * D);        // K rows per 1 KiB transfer
-  constexpr int PLOADS = kPage * KCH / 64;   // 1 KiB transfers per page
-  constexpr int WLOADS = kTilePages * PLOADS / kAttnWaves;  // transfers per wave, tensor and tile
-  static_assert(WLOADS >= 1 && PLOADS % WLOADS == 0, "a wave's copies stay inside one page");
-  __shared__ __attribute__((aligned(1024))) uint16_t sk0[kTileKeys * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sk1[kTileKeys * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sk2[kTileKeys * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sv0[kTileKeys * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sv1[kTileKeys * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sv2[kTileKeys * D];
+  constexpr int PCH = kPage * D * 2 / 1024;  // 1 KiB chunks per page
+  constexpr int WCH = kTilePages * PCH / kAttnWaves;  // chunks per wave, tensor and tile
+  static_assert(WCH >= 1 && PCH % WCH == 0, "a wave's chunks stay inside one page");
+  constexpr int kStage = kTileKeys * D;      // elements of one K or V stage
+  __shared__ __attribute__((aligned(1024))) uint16_t skv[6 * kStage];  // K stages 0-2, V stages 0-2
   __shared__ int spid[kMaxItemEntries];
   __shared__ __attribute__((aligned(16))) int spos[kMaxItemEntries];
-  __shared__ uint32_t swarm[kAttnThreads];  // sink of the L2 warm-up loads
   __shared__ int s_simd[kAttnWaves];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(a.plan);
@@ -188,7 +179,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
   const int lo_row = is_local ? local_lo(pos, mt.bq, mt.W) : 0;
   const int pos_min = mt.pos0, pos_max = mt.pos0 + mt.n_pos - 1;
   const int lo_max = is_local ? local_lo(pos_max, mt.bq, mt.W) : 0;
-  const uint8_t* mrow = kMask ? a.mask + ((size_t)mt.h * a.mask_rows + qrow) * a.mask_L + 8 * lg : nullptr;
 
   // the item's page table -> LDS (entries past the m-tile's end, or with an
   // invalid page id, become pid -1 / pos INT_MAX)
@@ -207,6 +197,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
     spid[x] = pid;
     spos[x] = ps;
   }
+
   // the two waves of each SIMD: the first joins set 0, the second set 1
   // (hardware register HW_ID, bits 5:4 = SIMD id)
   const int simd = __builtin_amdgcn_s_getreg(4 | (4 << 6) | (1 << 11));
@@ -224,57 +215,72 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
   for (int w = 0; w < wave; ++w) rank += s_simd[w] == simd;
   const int set = __builtin_amdgcn_readfirstlane(rank & 1);
 
-  // Copies. Transfer g = WLOADS wave + u of a tile moves 1 KiB of page
-  // g / PLOADS, so each wave copies inside one page (wave-uniform page id). A
-  // missing page (id -1) is copied from an all-zero page: its keys are masked
-  // by position and its zero V rows add nothing.
-  int koff[WLOADS], voff[WLOADS];
+  // Copies. Chunk g = WCH wave + u of a tile is 1 KiB of page g / PCH, so each
+  // wave copies inside one page (wave-uniform page id). Lane l moves 16 bytes
+  // to LDS byte 16 l of the chunk's kilobyte; which 16 bytes of the page it
+  // fetches is chosen so that the LDS layout comes out swizzled: K rows are
+  // token-major with their 16-byte chunks XOR-swizzled per row, V pages are
+  // d-major ([d][16 tokens]) with the two 16-byte halves of a row swapped on
+  // every other group of 8 d. Both operand reads below are then free of bank
+  // conflicts and full 16-byte reads. A missing page (id -1) is read from an
+  // all-zero page: its keys are masked by position and its zero V rows add
+  // nothing.
+  const int cpage = wave * WCH / PCH;  // this wave's page of every tile
+  constexpr int RPK = 1024 / (2 * D);  // K rows per kilobyte
+  int koff[WCH], voff[WCH];            // source byte offsets in the page
 #pragma unroll
-  for (int u = 0; u < WLOADS; ++u) {
-    const int part = (wave * WLOADS + u) % PLOADS;
+  for (int u = 0; u < WCH; ++u) {
+    const int part = (wave * WCH + u) % PCH;
     const int row = part * RPK + lane / KCH;  // K row inside the page
-    koff[u] = row * D + 8 * ((lane % KCH) ^ k_swz<D>(row));
-    // V pages are d-major ([d][16 tokens], 32 bytes per d): 16-byte half hs of
-    // row d lands at hs ^ ((d >> 3) & 1), so the operand reads below (32 rows d,
-    // both halves) hit distinct banks
+    koff[u] = 2 * (row * D + 8 * ((lane % KCH) ^ k_swz<D>(row)));
     const int c = part * 64 + lane, vd = c >> 1;
-    voff[u] = vd * kPage + 8 * ((c & 1) ^ ((vd >> 3) & 1));
+    voff[u] = 2 * (vd * kPage + 8 * ((c & 1) ^ ((vd >> 3) & 1)));
   }
-  const int cpage = wave * WLOADS / PLOADS;  // this wave's page of every tile
-  // buffer resource of one page (raw, 4 KiB at D = 128)
-  auto page_rsrc = [&](const uint16_t* page) __attribute__((always_inline)) {
-    return make_rsrc(page, kPage * D * 2);
+  auto pid_of = [&](int i) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane(spid[kTilePages * imin(i, T - 1) + cpage]);
   };
-  auto kpage_of = [&](int pid) __attribute__((always_inline)) { return pid < 0 ? a.zero_page : a.k_pool + (size_t)pid * kPage * D; };
-  auto vpage_of = [&](int pid) __attribute__((always_inline)) { return pid < 0 ? a.zero_page : a.v_pool + (size_t)pid * kPage * D; };
-  auto pid_of = [&](int i) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(spid[kTilePages * imin(i, T - 1) + cpage]); };
-  // Copies go through buffer loads (a page-sized buffer resource per source
-  // page): unlike global_load_lds they leave the compiler's LDS-read waits
-  // exact while a copy is in flight.
-  auto copy_k = [&](uint16_t* dst, const uint16_t* page) __attribute__((always_inline)) {
-    const buf_rsrc rs = page_rsrc(page);
+  // raw buffer resource over one page
+  auto page_rsrc = [&](const uint16_t* pool, int pid) __attribute__((always_inline)) {
+    const uint64_t addr = reinterpret_cast<uint64_t>(pid < 0 ? a.zero_page : pool + (size_t)pid * kPage * D);
+    return u32x4{(uint32_t)addr, (uint32_t)(addr >> 32) & 0xffffu, (uint32_t)(kPage * D * 2), (uint32_t)kBufferRsrcWord3};
+  };
+  const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(skv);  // LDS byte address
+  const uint32_t wave_dst = (uint32_t)(wave * WCH * 1024);
+  // one 16-byte-per-lane copy into LDS. Written as one asm statement so the
+  // compiler does not treat the LDS reads of other stages as waiting on it:
+  // completion is managed here (s_waitcnt vmcnt + barrier). The instruction
+  // has no register result.
+  auto dma = [&](uint32_t lds_byte, const u32x4& rs, int off) __attribute__((always_inline)) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_byte), "v"(off), "s"(rs)
+                 : "memory", "m0");
+  };
+  auto copy_k = [&](int pid, int stage) __attribute__((always_inline)) {  // K page `pid` into K stage `stage`
+    const u32x4 rs = page_rsrc(a.k_pool, pid);
+    const uint32_t dst = lds_base + (uint32_t)(stage * kStage * 2) + wave_dst;
 #pragma unroll
-    for (int u = 0; u < WLOADS; ++u) buffer_to_lds16(rs, &dst[(wave * WLOADS + u) * 512], 2 * koff[u]);
+    for (int u = 0; u < WCH; ++u) dma(dst + 1024 * u, rs, koff[u]);
   };
-  auto copy_v = [&](uint16_t* dst, const uint16_t* page) __attribute__((always_inline)) {
-    const buf_rsrc rs = page_rsrc(page);
+  auto copy_v = [&](int pid, int stage) __attribute__((always_inline)) {  // V page `pid` into V stage `stage`
+    const u32x4 rs = page_rsrc(a.v_pool, pid);
+    const uint32_t dst = lds_base + (uint32_t)((3 + stage) * kStage * 2) + wave_dst;
 #pragma unroll
-    for (int u = 0; u < WLOADS; ++u) buffer_to_lds16(rs, &dst[(wave * WLOADS + u) * 512], 2 * voff[u]);
+    for (int u = 0; u < WCH; ++u) dma(dst + 1024 * u, rs, voff[u]);
   };
-  // L2 warm-up of a tile: wave w loads one 4-byte word per 1/64 of the K (w
-  // even) or V (w odd) copy of its page, so that the copy two tiles later hits
-  // the cache. The words land in an LDS area that is never read.
-  const int warm_off = lane * (kPage * D / 32);  // bytes
-  const bool warm_v = (wave & 1) != 0;
-  auto touch = [&](int pid) __attribute__((always_inline)) {
-    buffer_to_lds4(page_rsrc(warm_v ? vpage_of(pid) : kpage_of(pid)), &swarm[wave * 64], warm_off);
-  };
+  constexpr int kCopyOps = 2 * WCH;  // vector memory operations of one iteration's copies
+  static_assert(3 * WCH < 16, "vmcnt immediate");
+  const char* lds = reinterpret_cast<const char*>(skv);
+  auto kstage = [&](int stage) __attribute__((always_inline)) { return lds + stage * (kStage * 2); };
+  auto vstage = [&](int stage) __attribute__((always_inline)) { return lds + (3 + stage) * (kStage * 2); };
 
-  // S^T operand: K row this lane feeds for key block 0 (slot permutation; block 1: +32)
+  // S^T operand: the K row this lane feeds for key block 0 (slot permutation;
+  // block 1: +32). The read of k-step ks sits at chunk (2 ks + lg) ^ swz of the
+  // row (one xor-add per read).
   const int krow0 = slot_key(lrow);
+  const int k_row_bytes = 2 * krow0 * D;
+  const int k_sw = 16 * (lg ^ k_swz<D>(krow0));  // same swizzle for rows krow0 and krow0 + 32
   // V^T operand: d-major page rows, this lane's row lrow of each 32-row d
   // block and its 8 keys lg of the page (swizzled half, as written by the copy)
-  const int v_lane = lrow * kPage + 8 * (lg ^ ((lrow >> 3) & 1));
+  const int v_lane_bytes = 2 * (lrow * kPage + 8 * (lg ^ ((lrow >> 3) & 1)));
 
   f32x16 o_acc[DB];
 #pragma unroll
@@ -284,71 +290,23 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
   // The running max m_run is an integer (or -inf), so a rescale factor is an
   // exact power of two.
   float m_run = -INFINITY, l_run = 0.f;
-  // P of the previous tile in bf16, the B operand of its PV product. The first
-  // MFMA step multiplies these zeros with the zeroed V stage 1.
-  bf16x8 pprev[4];
+  // P of the previous tile in bf16, the B operand of its PV product (zero
+  // before tile 0); the softmax of a tile overwrites each page's part after the
+  // PV product of the previous tile has read it
+  bf16x8 pk[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pprev[kk][j] = (__bf16)0.f;
-  f32x16 sc[2];   // S(i) from the MFMA step to the softmax step
-  int4 tpos_v;    // key positions of tile i's pages (read in its MFMA step)
-  // a rescale of O found due by a softmax step, applied before the next PV product
+    for (int j = 0; j < 8; ++j) pk[kk][j] = (__bf16)0.f;
+  f32x16 sc[2];  // S^T of the current tile (two 32-key blocks)
+  // a rescale of O found due by a softmax, applied before the next PV product
   float o_scale = 1.f;
   bool o_scale_due = false;
-
-  // stage buffers of tile i (stage i % 3, a compile-time index)
-  auto kst = [&](auto st) __attribute__((always_inline)) {
-    constexpr int S = decltype(st)::value % 3;
-    return S == 0 ? sk0 : S == 1 ? sk1 : sk2;
-  };
-  auto vst = [&](auto st) __attribute__((always_inline)) {
-    constexpr int S = decltype(st)::value % 3;
-    return S == 0 ? sv0 : S == 1 ? sv1 : sv2;
-  };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-
-  // K(0), K(1), V(0) before the loop; V(-1) (stage 2) is zero; page ids of
-  // this wave's page in tiles i+1 .. i+4 (wave-uniform, clamped to T-1)
-  int pid1 = pid_of(1), pid2 = pid_of(2), pid3 = pid_of(3), pid4 = pid_of(4);
-  {
-    const int pid0 = pid_of(0);
-    copy_k(sk0, kpage_of(pid0));
-    copy_k(sk1, kpage_of(pid1));
-    copy_v(sv0, vpage_of(pid0));
-  }
-  for (int e = tid * 8; e < kTileKeys * D; e += kAttnThreads * 8) *reinterpret_cast<u32x4*>(&sv2[e]) = u32x4{0, 0, 0, 0};
-  touch(pid2);
-  touch(pid3);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
 
   auto bar = [&]() __attribute__((always_inline)) {  // bare barrier; the empty asm statements keep LDS accesses on their side
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-  };
-  // at the end of slot 2i+1: this wave's copies of slot 2i-2 have landed (those
-  // of slot 2i, kCopyOps vector memory operations, may stay in flight; vector
-  // memory completes in order), then a barrier
-  constexpr int kCopyOps = 2 * WLOADS + 1;
-  static_assert(kCopyOps < 16, "vmcnt immediate");
-  auto wait_copies_bar = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0x0F70 | kCopyOps);
-    bar();
-  };
-  // copies of slot 2i: K(i+2) (near the end the last tile's K again, into an
-  // idle stage) and V(i+1), then the warm-up of tile i+4; next page id lookup
-  auto copies = [&](uint16_t* kdst, uint16_t* vdst, int i) __attribute__((always_inline)) {
-    copy_k(kdst, kpage_of(pid2));
-    copy_v(vdst, vpage_of(pid1));
-    touch(pid4);
-    pid1 = pid2;
-    pid2 = pid3;
-    pid3 = pid4;
-    pid4 = pid_of(i + 5);
   };
   auto rescale_o = [&]() __attribute__((always_inline)) {
     if (o_scale_due) {
@@ -359,161 +317,206 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
       o_scale_due = false;
     }
   };
-  // PV piece of page kk: O^T[b] += V^T(page kk) P^T(page kk) for every d block
-  auto pv_page = [&](const uint16_t* vbuf, const bf16x8& pk, int kk) __attribute__((always_inline)) {
+  // visibility of tile i (positions tp of its 4 pages): a tile that does not
+  // straddle a window edge, the causal diagonal or a missing page takes no
+  // mask work
+  auto mask_if_needed = [&](int i) __attribute__((always_inline)) {
+    const int4 tp = *reinterpret_cast<const int4*>(&spos[kTilePages * i]);
+    const int ps4[4] = {__builtin_amdgcn_readfirstlane(tp.x), __builtin_amdgcn_readfirstlane(tp.y),
+                        __builtin_amdgcn_readfirstlane(tp.z), __builtin_amdgcn_readfirstlane(tp.w)};
+    bool full = true;
+    if (!kMask) {
+      int kmin = INT_MAX, kmax = 0;
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vbuf[(kk * D + 32 * b) * kPage + v_lane]);
-      o_acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk, o_acc[b], 0, 0, 0);
+      for (int pp = 0; pp < 4; ++pp) {
+        full = full && ps4[pp] != INT_MAX;
+        kmin = imin(kmin, ps4[pp]);
+        kmax = imax(kmax, ps4[pp] == INT_MAX ? 0 : ps4[pp]);
+      }
+      full = full && kmax + kPage - 1 <= pos_min && (!is_local || kmin >= lo_max);
     }
-  };
-
-  // MFMA step of tile i (stage P = i % 3): S(i) = K(i) Q^T, O += V(i-1)^T P(i-1)
-  auto mfma_step = [&](auto par, int i) __attribute__((always_inline)) {
-    constexpr int P = decltype(par)::value;
-    const uint16_t* kcur = kst(par);
-    const uint16_t* vprev = vst(std::integral_constant<int, P + 2>{});
-    tpos_v = *reinterpret_cast<const int4*>(&spos[kTilePages * i]);
-    rescale_o();
+    if (kMask || !full) {
+      if (kMask) {
+        // bytes of keys ps + 8 lg .. + 7 of each page, this row
+        const uint8_t* mrow = a.mask + ((size_t)mt.h * a.mask_rows + qrow) * a.mask_L + 8 * lg;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int pp = 0; pp < 4; ++pp) {
+          const uint64_t mb = ps4[pp] != INT_MAX ? *reinterpret_cast<const uint64_t*>(mrow + ps4[pp]) : 0;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
+          for (int e = 0; e < 8; ++e) {
+            const int k = 8 * (pp & 1) + e;
+            sc[pp >> 1][k] = ((mb >> (8 * e)) & 0xffu) != 0 ? sc[pp >> 1][k] : -INFINITY;
+          }
+        }
+      } else {
+        // key j is visible iff lo_row <= j <= pos; a missing page (position
+        // INT_MAX) is placed far below every row's window
+        const unsigned span = (unsigned)(pos - lo_row);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+        for (int pp = 0; pp < 4; ++pp) {
+          const int ps = ps4[pp] == INT_MAX ? -(1 << 30) : ps4[pp];
+          const int d0 = ps + 8 * lg - lo_row;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int row = 32 * kb + krow0;
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&kcur[row * D + 8 * ((2 * ks + lg) ^ k_swz<D>(row))]);
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[kb], 0, 0, 0);
+          for (int e = 0; e < 8; ++e) {
+            const int k = 8 * (pp & 1) + e;
+            sc[pp >> 1][k] = (unsigned)(d0 + e) <= span ? sc[pp >> 1][k] : -INFINITY;
+          }
+        }
       }
     }
+  };
+  // K and V operand reads from LDS: K rows for S^T (the read of k-step ks
+  // sits at chunk (2 ks + lg) ^ swz of the row), V^T rows d-major
+  auto rd_k = [&](const char* kbuf, int kb, int ks) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(kbuf + k_row_bytes + 64 * D * kb + ((32 * ks) ^ k_sw));
+  };
+  auto rd_v = [&](const char* vbuf, int kk, int b) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(vbuf + v_lane_bytes + 2 * (kk * D + 32 * b) * kPage);
+  };
+  // matrix step of tile i: S(i) = K(i) Q^T, then O += V(i-1)^T P(i-1). Operand
+  // reads run kAhead ahead of the matrix instructions that use them.
+  auto mfma_step = [&](const char* kbuf, const char* vbuf) __attribute__((always_inline)) {
+    rescale_o();
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) pv_page(vprev, pprev[kk], kk);
-    // schedule: keep kAhead operand reads in flight ahead of the matrix
-    // instructions (each read is one MFMA's A operand), so that LDS latency
-    // hides behind the MFMA pipeline
-    constexpr int kOps = 2 * KS + 4 * DB, kAhead = 10;
-    if (kAhead > 0) {
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_k(kbuf, kb, ks), qf[ks], ks == 0 ? f32x16{} : sc[kb], 0, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+        o_acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_v(vbuf, kk, b), pk[kk], o_acc[b], 0, 0, 0);
+    constexpr int kOps = 2 * KS + 4 * DB, kAhead = 12;
     __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // DS reads
 #pragma unroll
     for (int m = 0; m < kOps - kAhead; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
-    }
   };
-
-  // softmax step of tile i: visibility, row max (lazy rescale: the running max
-  // moves only when a tile's max exceeds it by more than 2^8, and then to the
-  // integer above), P(i) in bf16 and the row sums
-  auto softmax_step = [&]() __attribute__((always_inline)) {
-    const int p0 = __builtin_amdgcn_readfirstlane(tpos_v.x), p1 = __builtin_amdgcn_readfirstlane(tpos_v.y);
-    const int p2 = __builtin_amdgcn_readfirstlane(tpos_v.z), p3 = __builtin_amdgcn_readfirstlane(tpos_v.w);
-    const bool all_valid = p0 != INT_MAX && p1 != INT_MAX && p2 != INT_MAX && p3 != INT_MAX;
-    const int kmin = imin(imin(p0, p1), imin(p2, p3));
-    const int kmax = imax(imax(p0 == INT_MAX ? 0 : p0, p1 == INT_MAX ? 0 : p1),
-                          imax(p2 == INT_MAX ? 0 : p2, p3 == INT_MAX ? 0 : p3)) + kPage - 1;
-    const bool full = all_valid && kmax <= pos_min && (!is_local || kmin >= lo_max);
-    if (kMask || !full) {  // the class rule masks only tiles that straddle a window edge
-      uint64_t mb[4] = {0, 0, 0, 0};  // mask mode: bytes of keys ps + 8 lg .. + 7 of each page
-      if (kMask) {
-        if (p0 != INT_MAX) mb[0] = *reinterpret_cast<const uint64_t*>(mrow + p0);
-        if (p1 != INT_MAX) mb[1] = *reinterpret_cast<const uint64_t*>(mrow + p1);
-        if (p2 != INT_MAX) mb[2] = *reinterpret_cast<const uint64_t*>(mrow + p2);
-        if (p3 != INT_MAX) mb[3] = *reinterpret_cast<const uint64_t*>(mrow + p3);
-      }
+  // softmax step of tile i: visibility, row max and the running max (lazy:
+  // it moves only when a tile's max exceeds it by more than 2^8, and then to
+  // the integer above, so a rescale factor is an exact power of two), P(i) in
+  // bf16, row sums of the unrounded probabilities in fp32
+  auto softmax_step = [&](int i) __attribute__((always_inline)) {
+    mask_if_needed(i);
+    float mx[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int pp = 2 * kb + (e >> 3);
-          const int ps = pp == 0 ? p0 : pp == 1 ? p1 : pp == 2 ? p2 : p3;
-          const int j = ps + 8 * lg + (e & 7);
-          const bool vis = kMask ? ((mb[pp] >> (8 * (e & 7))) & 0xffu) != 0
-                                 : ps != INT_MAX && j <= pos && j >= lo_row;
-          sc[kb][e] = vis ? sc[kb][e] : -INFINITY;
-        }
-    }
-    float tm[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 4; ++c) {  // four chains of three-input maxima over 8 values
       const f32x16& v = sc[c >> 1];
       const int o = 8 * (c & 1);
-      tm[c] = fmaxf(fmaxf(fmaxf(v[o], v[o + 1]), fmaxf(v[o + 2], v[o + 3])),
-                    fmaxf(fmaxf(v[o + 4], v[o + 5]), fmaxf(v[o + 6], v[o + 7])));
+      float t = fmaxf(fmaxf(v[o], v[o + 1]), v[o + 2]);
+      t = fmaxf(fmaxf(t, v[o + 3]), v[o + 4]);
+      t = fmaxf(fmaxf(t, v[o + 5]), v[o + 6]);
+      mx[c] = fmaxf(t, v[o + 7]);
     }
-    const float tmax = max_halves(fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3])));
+    const float tmax = max_halves(fmaxf(fmaxf(fmaxf(mx[0], mx[1]), mx[2]), mx[3]));
     const float m_tile = tmax * a.scale_log2;
     const bool grow = m_tile > m_run + kRescaleThreshold;
     const float m_new = grow ? ceilf(m_tile) : m_run;
+    // l and O move to the new max (O before the next PV product).
+    // Branch-free: from m_run = -inf the factor is 2^-200 = 0.
+    const float alpha = grow ? __builtin_amdgcn_ldexpf(1.f, (int)fmaxf(m_run - m_new, -200.f)) : 1.f;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};  // four partial row sums (short dependency chains)
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 pv;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sc[kk >> 1][8 * (kk & 1) + j], a.scale_log2, -m_use));
-        pprev[kk][j] = (__bf16)pv;
-        ls[j & 3] += pv;
+        const float x = __builtin_amdgcn_exp2f(fmaf(sc[kk >> 1][8 * (kk & 1) + j], a.scale_log2, -m_use));
+        pv[j] = (__bf16)x;
+        ls[j & 3] += x;
       }
-    // l moves to the new max now; O before the next PV product
-    const float alpha = grow ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(m_run - ceilf(m_tile)))) : 1.f;
+      pk[kk] = pv;
+    }
     l_run = l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
     m_run = m_new;
     o_scale = alpha;
     o_scale_due = __builtin_amdgcn_ballot_w64(grow) != 0;
   };
+  auto last_pv = [&](const char* vbuf) __attribute__((always_inline)) {
+    rescale_o();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+        o_acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_v(vbuf, kk, b), pk[kk], o_acc[b], 0, 0, 0);
+  };
+  // at the end of an odd slot: this wave's copies issued two slots before the
+  // last even slot have landed (those of the last even slot, kCopyOps vector
+  // memory operations, may stay in flight), then a barrier
+  auto wait_copies_bar = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kCopyOps);
+    bar();
+  };
 
+  // prologue: K(0), K(1), V(0) land before the first slot; V(-1) = 0 in V stage 2
+  copy_k(pid_of(0), 0);
+  copy_k(pid_of(1), 1);
+  copy_v(pid_of(0), 0);
+  for (int e = tid * 16; e < kStage * 2; e += kAttnThreads * 16)
+    *reinterpret_cast<u32x4*>(skv + 5 * kStage + e / 2) = u32x4{0, 0, 0, 0};
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+
+  // Slots alternate between the two sets: in slot 2i set 0 runs the matrix
+  // step of tile i while set 1 runs the softmax step of tile i-1; in slot 2i+1
+  // set 0 runs the softmax step of tile i while set 1 runs the matrix step of
+  // tile i. Each SIMD's matrix core then works for one of its waves while the
+  // other does vector work. At the start of slot 2i every wave issues the
+  // copies of K(i+2) and V(i+1) (stages of tile j: j % 3). The page id of the
+  // next K copy is read from LDS one tile ahead (its V copy reuses it a tile
+  // later), so no copy waits on an LDS read.
+  int st_m = 2, st_0 = 0, st_p = 1;  // stages of tiles i-1, i, i+1
+  auto rotate = [&]() __attribute__((always_inline)) {
+    const int t = st_m;
+    st_m = st_0;
+    st_0 = st_p;
+    st_p = t;
+  };
+  int pid_v = pid_of(1), pid_k = pid_of(2);  // pages of the next V and K copies
+  auto issue_copies = [&](int i) __attribute__((always_inline)) {  // K(i+2), V(i+1) of slot 2i
+    copy_k(pid_k, st_m);
+    copy_v(pid_v, st_p);
+    const int nxt = spid[kTilePages * imin(i + 3, T - 1) + cpage];  // K(i+3), read into a VGPR now
+    pid_v = pid_k;
+    return nxt;
+  };
   if (set == 0) {
-    // slot 2i: copies + MFMA step of tile i; slot 2i+1: softmax step of tile i
-    auto tile = [&](auto par, int i) __attribute__((always_inline)) {
-      constexpr int P = decltype(par)::value;
-      copies(kst(std::integral_constant<int, P + 2>{}), vst(std::integral_constant<int, P + 1>{}), i);
-      mfma_step(par, i);
+    for (int i = 0; i < T; ++i) {
+      mfma_step(kstage(st_0), vstage(st_m));
       bar();
-      softmax_step();
+      // (set 0 issues the copies of slot 2i in slot 2i+1, off its matrix step)
+      const int nxt = issue_copies(i);
+      softmax_step(i);
       wait_copies_bar();
-    };
-    for (int i = 0; i < T; i += 3) {
-      tile(S0{}, i);
-      if (i + 1 < T) tile(S1{}, i + 1);
-      if (i + 2 < T) tile(S2{}, i + 2);
+      pid_k = __builtin_amdgcn_readfirstlane(nxt);
+      rotate();
     }
   } else {
-    // slot 0: copies of tile 0; then slot 2i+1: MFMA step of tile i; slot
-    // 2i+2: copies of tile i+1 + softmax step of tile i
-    copies(sk2, sv1, 0);
+    pid_k = __builtin_amdgcn_readfirstlane(issue_copies(0));
     bar();
-    auto tile = [&](auto par, int i) __attribute__((always_inline)) {
-      constexpr int P = decltype(par)::value;
-      mfma_step(par, i);
+    for (int i = 0; i < T; ++i) {
+      mfma_step(kstage(st_0), vstage(st_m));
       wait_copies_bar();
       if (i + 1 < T) {
-        copies(kst(std::integral_constant<int, P + 3>{}), vst(std::integral_constant<int, P + 2>{}), i + 1);
-        softmax_step();
+        rotate();
+        const int nxt = issue_copies(i + 1);
+        softmax_step(i);
         bar();
+        pid_k = __builtin_amdgcn_readfirstlane(nxt);
       } else {
-        softmax_step();
+        softmax_step(i);
+        rotate();
       }
-    };
-    for (int i = 0; i < T; i += 3) {
-      tile(S0{}, i);
-      if (i + 1 < T) tile(S1{}, i + 1);
-      if (i + 2 < T) tile(S2{}, i + 2);
     }
   }
-  // the last copies and warm-up loads land before the work-group may end
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  {  // the last tile's PV product: V(T-1) sits in stage (T-1) % 3, landed before the last barrier
-    rescale_o();
-    const int last = (T - 1) % 3;
-    const uint16_t* vlast = last == 0 ? sv0 : last == 1 ? sv1 : sv2;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) pv_page(vlast, pprev[kk], kk);
-  }
+  // the PV product of tile T-1 (V(T-1) has landed; st_m is its stage)
+  last_pv(vstage(st_m));
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the last (unused) copies land before the work-group may end
 
   const float l_row = l_run + __shfl_xor(l_run, 32);
   // O leaves through LDS: the lane's O^T fragment (its row, 4-wide d groups)
@@ -524,8 +527,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
   const float inv = l_row > 0.f ? 1.f / l_row : 0.f;  // a chunk may hold no key of a row: O_c = 0, l_c = 0
   __syncthreads();  // every wave's last PV product has read its V stage
   constexpr int OCH = D / 8;  // 16-byte chunks per row
-  uint16_t* ostage = ((wave >> 1) == 0 ? sk0 : (wave >> 1) == 1 ? sk1 : (wave >> 1) == 2 ? sk2 : sv0) +
-                     (wave & 1) * 32 * D;
+  uint16_t* ostage = skv + wave * 32 * D;
 #pragma unroll
   for (int b = 0; b < DB; ++b)
 #pragma unroll
