@@ -23,6 +23,7 @@ GLOBAL, LOCAL, RETRIEVAL, DENSE = 0, 1, 2, 3
 EXPORTS = [
     "segkv_status_string", "segkv_last_error", "segkv_plan_sizes", "segkv_build_pages",
     "segkv_visible_spans", "rope_relocate", "segpaged_attn_prefill", "segpaged_attn_prefill_masked",
+    "segpaged_attn_prefill_noalloc",
     "token_importance_topk",
     "segkv_decode_workspace_size", "segpaged_attn_decode",
     "segkv_topk_select", "sparse_ffn_workspace_size", "sparse_ffn_swiglu",
@@ -79,6 +80,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rope_relocate": ([P, P, P, P, I64, I64, P, P, P, I32, I32, I32, F64, P], I32),
         "segpaged_attn_prefill": ([P, P, P, P, P, I64, P, P, P, SZ, F32, P, P, P, SZ, P], I32),
         "segpaged_attn_prefill_masked": ([P, P, P, P, P, I64, P, P, P, SZ, F32, P, I64, P, P, P, SZ, P], I32),
+        "segpaged_attn_prefill_noalloc": ([P, P, P, P, P, I64, P, P, P, SZ, F32, P, P, P], I32),
         "segkv_decode_workspace_size": ([P, P, P], I32),
         "segpaged_attn_decode": ([P, P, P, P, P, P, P, P, I64, P, P, P, F32, P, P, P, SZ, P], I32),
         "token_importance_topk": ([P, P, P, P, P, P, I64, P, P, P, P, SZ, P, F32, I32, P, P, P, P, SZ, P], I32),
@@ -201,6 +203,16 @@ def segpaged_attn_prefill(d: Dims, meta: HostMeta, q, k_pool, v_pool, page_ids, 
         ctypes.byref(d), ctypes.byref(ms), _ptr(q), _ptr(k_pool), _ptr(v_pool), k_pool.shape[0], _ptr(page_ids),
         _ptr(page_pos), _ptr(plan), plan.numel() * plan.element_size(), float(softmax_scale), _ptr(out),
         _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def segpaged_attn_prefill_noalloc(d: Dims, meta: HostMeta, q, k_pool, v_pool, page_ids, page_pos, plan,
+                                  softmax_scale: float, out, lse=None, stream=None):
+    lib = load()
+    ms = meta.struct()
+    _check("segpaged_attn_prefill_noalloc", lib.segpaged_attn_prefill_noalloc(
+        ctypes.byref(d), ctypes.byref(ms), _ptr(q), _ptr(k_pool), _ptr(v_pool), k_pool.shape[0], _ptr(page_ids),
+        _ptr(page_pos), _ptr(plan), plan.numel() * plan.element_size(), float(softmax_scale), _ptr(out),
+        _ptr(lse), _stream(stream)))
 
 
 def segkv_decode_workspace_size(d: Dims, meta: HostMeta) -> int:

@@ -649,6 +649,34 @@ const uint16_t* zero_page_address() {
   return addr[dev];
 }
 
+// Split-KV partials buffer of segpaged_attn_prefill_noalloc: a fixed device
+// array, so that entry point calls no allocator. Each device holds its own
+// copy for the life of the process.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current (the host-side name is only a stand-in).
+char* scratch_address() {
+  static std::mutex mu;
+  static char* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    char* p = nullptr;
+    if (hipGetSymbolAddress((void**)&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
 }  // namespace
 }  // namespace segkv
 
@@ -658,7 +686,8 @@ namespace {
 int32_t attn_prefill(const segkv_dims* dims, const segkv_meta* meta_host, const void* q, const void* k_pool,
                      const void* v_pool, int64_t pool_pages, const int32_t* page_ids_dev, const int32_t* page_pos_dev,
                      const void* plan_dev, size_t plan_bytes, float softmax_scale, const uint8_t* mask,
-                     int64_t mask_L, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                     int64_t mask_L, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                     bool fixed_scratch = false) {
   HostPlan hp;
   int32_t st = compute_host_plan(dims, meta_host, &hp);
   if (st != SEGKV_OK) return st;
@@ -670,9 +699,18 @@ int32_t attn_prefill(const segkv_dims* dims, const segkv_meta* meta_host, const 
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) || !aligned16(plan_dev))
     return fail(SEGKV_ERR_ALIGNMENT, "q, pools, out and plan must be 16-byte aligned");
   if (plan_bytes < hp.plan_bytes) return fail(SEGKV_ERR_WORKSPACE, "plan buffer too small");
-  if (workspace_bytes < hp.workspace_bytes)
+  if (workspace_bytes < hp.workspace_bytes) {
+    if (fixed_scratch)
+      return fail(SEGKV_ERR_WORKSPACE, "layout needs " + std::to_string(hp.workspace_bytes) +
+                                           " bytes of split-KV partials, above the fixed " +
+                                           std::to_string(workspace_bytes) + "-byte scratch of the no-alloc entry");
     return fail(SEGKV_ERR_WORKSPACE, "attention workspace " + std::to_string(workspace_bytes) + " < " +
                                          std::to_string(hp.workspace_bytes));
+  }
+  if (fixed_scratch) {
+    workspace = scratch_address();
+    if (workspace == nullptr) return fail(SEGKV_ERR_HIP, "hipGetSymbolAddress of the attention scratch failed");
+  }
   if (hp.workspace_bytes > 0 && (!workspace || !aligned16(workspace)))
     return fail(SEGKV_ERR_ALIGNMENT, "workspace must be a 16-byte aligned device buffer");
   if (hp.n_items == 0) return SEGKV_OK;
@@ -726,6 +764,21 @@ extern "C" int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_met
   clear_error();
   return attn_prefill(dims, meta_host, q, k_pool, v_pool, pool_pages, page_ids_dev, page_pos_dev, plan_dev,
                       plan_bytes, softmax_scale, nullptr, 0, out, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" int32_t segpaged_attn_prefill_noalloc(const segkv_dims* dims, const segkv_meta* meta_host,
+                                                 const void* q, const void* k_pool, const void* v_pool,
+                                                 int64_t pool_pages, const int32_t* page_ids_dev,
+                                                 const int32_t* page_pos_dev, const void* plan_dev,
+                                                 size_t plan_bytes, float softmax_scale, void* out, float* lse,
+                                                 void* stream) {
+  clear_error();
+  // the scratch address is looked up after the size checks; every split chunk
+  // writes its whole partial slot before the combine reads it, so the scratch
+  // needs no clearing between calls
+  return attn_prefill(dims, meta_host, q, k_pool, v_pool, pool_pages, page_ids_dev, page_pos_dev, plan_dev,
+                      plan_bytes, softmax_scale, nullptr, 0, out, lse, nullptr, kNoAllocScratchBytes, stream,
+                      true);
 }
 
 extern "C" int32_t segpaged_attn_prefill_masked(const segkv_dims* dims, const segkv_meta* meta_host, const void* q,

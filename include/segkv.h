@@ -188,6 +188,24 @@ int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_meta* meta_hos
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * segpaged_attn_prefill without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Arguments, layouts and results are those
+ * of segpaged_attn_prefill. The split-KV partials live in a fixed 64 MiB
+ * device array inside the library (one per GPU, held until the process ends);
+ * a layout whose attn_workspace_bytes exceeds 64 MiB (67108864) is rejected
+ * with SEGKV_ERR_WORKSPACE before any launch. Calls no allocator. All calls
+ * on one GPU share that array: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and give wrong results; calls ordered on
+ * one stream are safe.
+ */
+int32_t segpaged_attn_prefill_noalloc(const segkv_dims* dims, const segkv_meta* meta_host,
+                                      const void* q, const void* k_pool, const void* v_pool, int64_t pool_pages,
+                                      const int32_t* page_ids_dev, const int32_t* page_pos_dev,
+                                      const void* plan_dev, size_t plan_bytes,
+                                      float softmax_scale, void* out, float* lse, void* stream);
+
+/*
  * The same attention with an explicit mask in place of the class rule: the
  * tuned form of the masked-dense comparator (paooo.com "RedKnot的技术原理":
  * the fused kernel replaces a dense layout plus mask). Every key tile of
