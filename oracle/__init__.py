@@ -31,7 +31,7 @@ from .visibility import (visible_brute, visible_intervals, page_table, page_tabl
 from .attention import attention, attention_brute  # noqa: F401
 from .decode import decode, decode_brute  # noqa: F401
 from .importance import importance, topk_select  # noqa: F401
-from .ffn import sparse_ffn  # noqa: F401
+from .ffn import sparse_ffn, swiglu_activation  # noqa: F401
 from .dense import dense_layout, masked_dense  # noqa: F401
 from .stack import shallow_layout, stack  # noqa: F401
 from .layer import row_positions, qkv_rope, append_query_kv, out_proj_residual, layer  # noqa: F401

@@ -21,6 +21,12 @@ def _silu(x):
     return x / (1.0 + np.exp(-x))
 
 
+def swiglu_activation(hidden_bits, idx, w_gate_bits, w_up_bits):
+    """silu(W_gate h) * (W_up h) for the rows idx, fp64, before its bf16 rounding."""
+    X = bf16_bits_to_f64(hidden_bits)[np.asarray(idx, dtype=np.int64)]
+    return _silu(X @ bf16_bits_to_f64(w_gate_bits).T) * (X @ bf16_bits_to_f64(w_up_bits).T)
+
+
 def sparse_ffn(hidden_bits, idx, w_gate_bits, w_up_bits, w_down_bits):
     """Returns the fp64 output rows [n, hidden] (before the final bf16 store)."""
     H = bf16_bits_to_f64(hidden_bits)
@@ -28,10 +34,6 @@ def sparse_ffn(hidden_bits, idx, w_gate_bits, w_up_bits, w_down_bits):
     idx = np.asarray(idx, dtype=np.int64)
     if len(idx) == 0:
         return out
-    Wg = bf16_bits_to_f64(w_gate_bits)
-    Wu = bf16_bits_to_f64(w_up_bits)
-    Wd = bf16_bits_to_f64(w_down_bits)
-    X = H[idx]
-    a = round_bf16(_silu(X @ Wg.T) * (X @ Wu.T))
-    out[idx] = X + a @ Wd.T
+    a = round_bf16(swiglu_activation(hidden_bits, idx, w_gate_bits, w_up_bits))
+    out[idx] = H[idx] + a @ bf16_bits_to_f64(w_down_bits).T
     return out

@@ -71,7 +71,7 @@ def test_valid_layout_sizes():
     (dict(Hq=6), -1),                                   # Hq % Hkv != 0
     (dict(D=96), -2),                                   # unsupported head_dim
     (dict(P=32), -2),                                   # unsupported page size
-    (dict(Hq=12, Hkv=4), -2),                           # group 3 does not divide 128
+    (dict(Hq=12, Hkv=4), -2),                           # group 3 does not divide 256
     (dict(R=0), -1),
     (dict(head_class=[0, 7, 1, 3]), -1),                # unknown class
     (dict(window=[0, 0, 32, 0]), -1),                   # LOCAL with window 0

@@ -21,7 +21,7 @@ import oracle
 import workloads
 import dataclasses
 
-from gpu_util import Dev, assert_attn_close, bf16, bits, layer_for, sample_rows
+from gpu_util import Dev, assert_attn_close, bf16, bits, layer_for
 from head_aware_paged_amd import masked_dense_attn, segkv_masked_dense_workspace_size
 
 pytestmark = pytest.mark.gpu
@@ -75,15 +75,25 @@ def test_random_mask(T, Hq, Hkv, D, L):
     check(f"random T={T} D={D}", ob, lse, O, Ls)
 
 
-def test_mistral_32k_sampled():
-    w = workloads.mistral_32k()
-    print("case mistral7b_32k: masked dense (class mask), sampled rows", flush=True)
-    L = 33280
-    K, V, mask = oracle.dense_layout(w, L)
-    ob, lse = run_dense(w.q, K, V, mask)
-    rows = sample_rows(w, per_request=16)
-    O, Ls = oracle.masked_dense(w.q[rows], K, V, np.ascontiguousarray(mask[:, rows]))
-    assert_attn_close(ob[rows], lse[rows], O, Ls, name="mistral7b_32k masked dense")
+_MISTRAL_DENSE = {}
+
+
+def _mistral_dense():
+    """The 32K layout in dense form (L = 33280) and the oracle on every row,
+    computed once for both dense-layout tests."""
+    if not _MISTRAL_DENSE:
+        w = workloads.mistral_32k()
+        K, V, mask = oracle.dense_layout(w, 33280)
+        O, Ls = oracle.masked_dense(w.q, K, V, mask)
+        _MISTRAL_DENSE.update(w=w, K=K, V=V, mask=mask, O=O, L=Ls)
+    return _MISTRAL_DENSE
+
+
+def test_mistral_32k_all_rows():
+    print("case mistral7b_32k: masked dense (class mask), all rows", flush=True)
+    m = _mistral_dense()
+    ob, lse = run_dense(m["w"].q, m["K"], m["V"], m["mask"])
+    assert_attn_close(ob, lse, m["O"], m["L"], name="mistral7b_32k masked dense")
 
 
 def run_masked_prefill(w, mask):
@@ -133,12 +143,8 @@ def test_masked_prefill_random_causal_mask():
     assert_attn_close(ob, lse, O, Ls, name="g4_d128 masked prefill random")
 
 
-def test_masked_prefill_mistral_32k_sampled():
-    w = workloads.mistral_32k()
-    print("case mistral7b_32k: masked prefill (class mask, dense tables), sampled rows", flush=True)
-    L = 33280
-    K, V, mask = oracle.dense_layout(w, L)
-    ob, lse = run_masked_prefill(w, mask)
-    rows = sample_rows(w, per_request=16)
-    O, Ls = oracle.masked_dense(w.q[rows], K, V, np.ascontiguousarray(mask[:, rows]))
-    assert_attn_close(ob[rows], lse[rows], O, Ls, name="mistral7b_32k masked prefill")
+def test_masked_prefill_mistral_32k_all_rows():
+    print("case mistral7b_32k: masked prefill (class mask, dense tables), all rows", flush=True)
+    m = _mistral_dense()
+    ob, lse = run_masked_prefill(m["w"], m["mask"])
+    assert_attn_close(ob, lse, m["O"], m["L"], name="mistral7b_32k masked prefill")

@@ -1,7 +1,17 @@
 """GPU: token-selective SwiGLU FFN vs the fp64 oracle.
 
-Unselected rows must be bit-identical; selected rows within ulp_bf16(ref) +
-1e-3 of the oracle (which rounds the activation to bf16 at the same point).
+Unselected rows must be bit-identical. Selected rows: the kernel forms the
+activation a_j = silu(g_j) u_j in fp32 and the oracle in fp64, and both round
+it to bf16, so an activation lying next to a bf16 rounding midpoint may round
+to the neighbouring value on one side only (a "flip", one bf16 step s_j). The
+bound per output element i is therefore
+    |out_i - ref_i| <= ulp_bf16(ref_i) + sum_{j near a midpoint} |W_down[i, j]| s_j + 1e-4,
+where ulp_bf16(ref_i) covers the final bf16 store (half a step, either
+binade), the sum covers every possible flip, and 1e-4 the fp32 sums of the
+down projection. "Near" means within 2^-18 |a_j| + 2^-16 of the midpoint:
+fp32 evaluation of the 4096-long gate/up dot products of these unit-variance
+inputs moves a_j by well under 1e-5 (6.9e-6 at most in an fp32 emulation of
+512 rows of the 8K case), and the window is twice that.
 """
 import numpy as np
 import pytest
@@ -23,14 +33,26 @@ def run_ffn(d, idx):
     return bits(hid)
 
 
-def check(d, idx, got, rows=None):
+def flip_allowance(d, rows):
+    """Per output element, the sum of |W_down| times the bf16 step over the
+    activations that lie near a rounding midpoint."""
+    pre = oracle.swiglu_activation(d["hidden"], rows, d["w_gate"], d["w_up"])
+    a = oracle.round_bf16(pre)
+    b = oracle.f64_to_bf16_bits(a).astype(np.int32)
+    toward = np.where((b & 0x7FFF) == 0, b + 1, np.where(np.abs(pre) > np.abs(a), b + 1, b - 1))
+    nbr = oracle.bf16_bits_to_f64(toward.astype(np.uint16))
+    near = np.abs(pre - (a + nbr) / 2) <= 2.0 ** -18 * np.abs(pre) + 2.0 ** -16
+    return (near * np.abs(nbr - a)) @ np.abs(oracle.bf16_bits_to_f64(d["w_down"])).T
+
+
+def check(d, idx, got):
     sel = np.asarray(idx)
-    rows = sel if rows is None else rows
-    ref = oracle.sparse_ffn(d["hidden"], rows, d["w_gate"], d["w_up"], d["w_down"])
-    g = oracle.bf16_bits_to_f64(got[rows])
-    err = np.abs(g - ref[rows])
-    bound = oracle.ulp_bf16(ref[rows]) + 1e-3
-    print(f"FFN max err {err.max():.3e}, max err/bound {(err / bound).max():.3f}", flush=True)
+    ref = oracle.sparse_ffn(d["hidden"], sel, d["w_gate"], d["w_up"], d["w_down"])
+    g = oracle.bf16_bits_to_f64(got[sel])
+    err = np.abs(g - ref[sel])
+    bound = oracle.ulp_bf16(ref[sel]) + flip_allowance(d, sel) + 1e-4
+    print(f"FFN max err {err.max():.3e}, max err/bound {(err / bound).max():.3f}, "
+          f"mean err {err.mean():.3e}", flush=True)
     assert np.all(err <= bound)
     rest = np.setdiff1d(np.arange(d["hidden"].shape[0]), sel)
     assert np.array_equal(got[rest], d["hidden"][rest])
@@ -45,11 +67,10 @@ def test_small(n, h, inter, k):
     check(d, idx, got)
 
 
-def test_full_8k_selected_rows():
+def test_full_8k_all_selected_rows():
     w = workloads.sparse_ffn_8k()
     print("case sparse_ffn_8k: FFN on 2048 selected rows", flush=True)
     d = dict(hidden=w.hidden, w_gate=w.w_gate, w_up=w.w_up, w_down=w.w_down)
     idx = np.sort(np.random.default_rng(1).choice(8192, size=2048, replace=False)).astype(np.int32)
     got = run_ffn(d, idx)
-    rows = idx[np.random.default_rng(2).choice(2048, size=12, replace=False)]
-    check(d, idx, got, rows=rows)
+    check(d, idx, got)

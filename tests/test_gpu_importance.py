@@ -61,6 +61,17 @@ def test_importance_topk_8k():
     assert abs(imp.astype(np.float64).sum() - 32 * 64) < 1e-2
 
 
+@pytest.mark.parametrize("name", ["mistral7b_32k", "qwen3_32b_varlen"])
+def test_importance_topk_full_size(name):
+    """The attention layouts at full size: importance over each request's last
+    64 rows, top 25 % of its keys (the benchmark step's setting)."""
+    w = workloads.make(name)
+    print(f"case {name}: importance + top-k at full size", flush=True)
+    k = [w.context_len(r) // 4 for r in range(w.num_requests)]
+    imp, idx = run(w, 64, k)
+    check(w, imp, idx, 64, k)
+
+
 def test_zero_q_selects_lowest_indices():
     w = workloads.sparse_ffn_8k(with_ffn=False)
     w.q[:] = 0
