@@ -69,7 +69,11 @@ __device__ __forceinline__ int slot_key(int slot) {
   return 16 * (a >> 1) + 8 * g + 4 * (a & 1) + b;
 }
 
-constexpr int kMaxItemEntries = kTilePages * kMaxChunkTiles;  // table entries of one item
+// An item's page table sits in LDS as a ring of kRingTiles tiles: tile t at
+// entry kTilePages * (t % kRingTiles). Items longer than the ring refill the
+// half they have finished with, 128 tiles at a time.
+constexpr int kRingTiles = 256;
+constexpr int kRingEntries = kTilePages * kRingTiles;
 
 // Source of the copies of a missing page: zero K rows (masked by position
 // anyway) and zero V rows, so nothing has to be cleared in LDS. Kernels get its
@@ -149,8 +153,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
   static_assert(WCH >= 1 && PCH % WCH == 0, "a wave's chunks stay inside one page");
   constexpr int kStage = kTileKeys * D;      // elements of one K or V stage
   __shared__ __attribute__((aligned(1024))) uint16_t skv[6 * kStage];  // K stages 0-2, V stages 0-2
-  __shared__ int spid[kMaxItemEntries];
-  __shared__ __attribute__((aligned(16))) int spos[kMaxItemEntries];
+  __shared__ int spid[kRingEntries];
+  __shared__ __attribute__((aligned(16))) int spos[kRingEntries];
   __shared__ int s_simd[kAttnWaves];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(a.plan);
@@ -180,10 +184,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
   const int pos_min = mt.pos0, pos_max = mt.pos0 + mt.n_pos - 1;
   const int lo_max = is_local ? local_lo(pos_max, mt.bq, mt.W) : 0;
 
-  // the item's page table -> LDS (entries past the m-tile's end, or with an
-  // invalid page id, become pid -1 / pos INT_MAX)
+  // the item's page table -> LDS ring (entries past the m-tile's end, or with
+  // an invalid page id, become pid -1 / pos INT_MAX); the first kRingTiles
+  // tiles now, later ones by stage_table
   const int e_lo = mt.e_begin + kTilePages * t_lo;
-  for (int x = tid; x < kTilePages * T; x += kAttnThreads) {
+  auto stage_entry = [&](int x) __attribute__((always_inline)) {  // entry x of the item
     const int e = e_lo + x;
     int pid = -1, ps = INT_MAX;
     if (e < mt.e_end) {
@@ -194,9 +199,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
         ps = INT_MAX;
       }
     }
-    spid[x] = pid;
-    spos[x] = ps;
-  }
+    spid[x % kRingEntries] = pid;
+    spos[x % kRingEntries] = ps;
+  };
+  for (int x = tid; x < kTilePages * imin(T, kRingTiles); x += kAttnThreads) stage_entry(x);
 
   // the two waves of each SIMD: the first joins set 0, the second set 1
   // (hardware register HW_ID, bits 5:4 = SIMD id)
@@ -237,7 +243,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
     voff[u] = 2 * (vd * kPage + 8 * ((c & 1) ^ ((vd >> 3) & 1)));
   }
   auto pid_of = [&](int i) __attribute__((always_inline)) {
-    return __builtin_amdgcn_readfirstlane(spid[kTilePages * imin(i, T - 1) + cpage]);
+    return __builtin_amdgcn_readfirstlane(spid[kTilePages * (imin(i, T - 1) % kRingTiles) + cpage]);
   };
   // raw buffer resource over one page
   auto page_rsrc = [&](const uint16_t* pool, int pid) __attribute__((always_inline)) {
@@ -321,7 +327,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
   // straddle a window edge, the causal diagonal or a missing page takes no
   // mask work
   auto mask_if_needed = [&](int i) __attribute__((always_inline)) {
-    const int4 tp = *reinterpret_cast<const int4*>(&spos[kTilePages * i]);
+    const int4 tp = *reinterpret_cast<const int4*>(&spos[kTilePages * (i % kRingTiles)]);
     const int ps4[4] = {__builtin_amdgcn_readfirstlane(tp.x), __builtin_amdgcn_readfirstlane(tp.y),
                         __builtin_amdgcn_readfirstlane(tp.z), __builtin_amdgcn_readfirstlane(tp.w)};
     bool full = true;
@@ -481,9 +487,21 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
   auto issue_copies = [&](int i) __attribute__((always_inline)) {  // K(i+2), V(i+1) of slot 2i
     copy_k(pid_k, st_m);
     copy_v(pid_v, st_p);
-    const int nxt = spid[kTilePages * imin(i + 3, T - 1) + cpage];  // K(i+3), read into a VGPR now
+    const int nxt = spid[kTilePages * (imin(i + 3, T - 1) % kRingTiles) + cpage];  // K(i+3), read into a VGPR now
     pid_v = pid_k;
     return nxt;
+  };
+  // Ring refill: the table reads of iteration i (either set) stay within
+  // tiles i-2 .. i+5, so at i = 128 k + 64 (k >= 1) the half holding tiles
+  // 128 (k-1) .. 128 k - 1 is finished with; every thread, in its set's
+  // iteration i, writes its entries of tiles 128 (k+1) .. 128 (k+1) + 127 into
+  // it, first read some 60 iterations (and barriers) later.
+  auto stage_table = [&](int i) __attribute__((always_inline)) {
+    if (i >= kRingTiles - 64 && (i & 127) == 64 && (i & ~127) + 128 < T) {
+      const int t0 = (i & ~127) + 128;
+      const int x_end = kTilePages * imin(t0 + 128, T);
+      for (int x = kTilePages * t0 + tid; x < x_end; x += kAttnThreads) stage_entry(x);
+    }
   };
   if (set == 0) {
     for (int i = 0; i < T; ++i) {
@@ -491,6 +509,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
       bar();
       // (set 0 issues the copies of slot 2i in slot 2i+1, off its matrix step)
       const int nxt = issue_copies(i);
+      stage_table(i);
       softmax_step(i);
       wait_copies_bar();
       pid_k = __builtin_amdgcn_readfirstlane(nxt);
@@ -502,6 +521,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
     for (int i = 0; i < T; ++i) {
       mfma_step(kstage(st_0), vstage(st_m));
       wait_copies_bar();
+      stage_table(i);
       if (i + 1 < T) {
         rotate();
         const int nxt = issue_copies(i + 1);
@@ -651,8 +671,11 @@ const uint16_t* zero_page_address() {
 
 // Split-KV partials buffer of segpaged_attn_prefill_noalloc: a fixed device
 // array, so that entry point calls no allocator. Each device holds its own
-// copy for the life of the process.
-constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+// copy for the life of the process. Its size is the most any layout needs on
+// a part with up to 256 compute units: at most kMaxItemRounds x 256 work items,
+// each with one D = 128 partial (bf16 O rows + fp32 m, l of 256 rows).
+constexpr size_t kNoAllocScratchBytes = (size_t)kMaxItemRounds * 256 * (kMRows * 128 * 2 + kMRows * 2 * 4);
+static_assert(kNoAllocScratchBytes == 69206016, "66 MiB");
 static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
 
 // Device address of `scratch` on the current device, looked up once per device

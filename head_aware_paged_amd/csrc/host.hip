@@ -122,7 +122,9 @@ static int64_t lpt_makespan(std::vector<int>& sizes, int bins) {
 }
 
 // Chunk cap S (tiles per work item): balance items over the resident slots
-// while keeping the number of split-KV partials small.
+// while keeping the number of split-KV partials small. Splits serve the
+// balance only (at most 4 rounds of slots), so the partials are bounded by
+// the slot count, not by query rows x keys.
 static int choose_chunk_tiles(const std::vector<int>& tiles, int slots) {
   int64_t total = 0;
   int tmax = 1;
@@ -135,9 +137,9 @@ static int choose_chunk_tiles(const std::vector<int>& tiles, int slots) {
     for (int t : tiles) n += num_chunks(t, S);
     return n;
   };
-  int best_S = std::min(tmax, kMaxChunkTiles);
+  int best_S = tmax;
   double best_cost = 1e300;
-  for (int rounds = 1; rounds <= 4; ++rounds) {
+  for (int rounds = 1; rounds <= kMaxItemRounds; ++rounds) {
     const int64_t target = (int64_t)rounds * slots;
     int lo = (int)std::max<int64_t>(1, (total + target - 1) / target), hi = tmax;
     if (lo > hi) lo = hi;
@@ -145,7 +147,7 @@ static int choose_chunk_tiles(const std::vector<int>& tiles, int slots) {
       int mid = lo + (hi - lo) / 2;
       if (items_for(mid) <= target) hi = mid; else lo = mid + 1;
     }
-    const int S = std::min(lo, kMaxChunkTiles);
+    const int S = lo;
     std::vector<int> sizes;
     int64_t partials = 0;
     for (int t : tiles) {

@@ -27,7 +27,7 @@ constexpr int kPage = 16;          // tokens per page
 constexpr int kTilePages = 4;      // pages per attention key tile
 constexpr int kTileKeys = kPage * kTilePages;
 constexpr int kMRows = 256;        // query rows per attention work-group (G heads x 256/G positions)
-constexpr int kMaxChunkTiles = 256;  // key tiles per work item (its page table is staged in LDS)
+constexpr int kMaxItemRounds = 4;  // attention work items are at most this many rounds of resident slots
 constexpr int kClassGlobal = 0, kClassLocal = 1, kClassRetrieval = 2, kClassDense = 3;
 
 SEGKV_HD int cdiv(int a, int b) { return (a + b - 1) / b; }

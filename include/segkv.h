@@ -191,10 +191,12 @@ int32_t segpaged_attn_prefill(const segkv_dims* dims, const segkv_meta* meta_hos
  * segpaged_attn_prefill without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc). Arguments, layouts and results are those
- * of segpaged_attn_prefill. The split-KV partials live in a fixed 64 MiB
- * device array inside the library (one per GPU, held until the process ends);
- * a layout whose attn_workspace_bytes exceeds 64 MiB (67108864) is rejected
- * with SEGKV_ERR_WORKSPACE before any launch. Calls no allocator. All calls
+ * of segpaged_attn_prefill. The split-KV partials live in a fixed device
+ * array of 69206016 bytes (66 MiB) inside the library (one per GPU, held
+ * until the process ends). That is the most attn_workspace_bytes can be on a
+ * GPU with up to 256 compute units (the MI355X has 256), so there every
+ * layout fits; elsewhere a layout needing more is rejected with
+ * SEGKV_ERR_WORKSPACE before any launch. Calls no allocator. All calls
  * on one GPU share that array: calls that overlap in time on one GPU (other
  * streams, other host threads) race and give wrong results; calls ordered on
  * one stream are safe.

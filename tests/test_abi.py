@@ -120,17 +120,11 @@ def test_attention_validation():
     assert lib.segpaged_attn_prefill(*args(plan_bytes=8)) == -5
     bad = hk.dims(1, 8, 4, 64, 16, 3)   # num_segments disagrees with seg_indptr
     assert lib.segpaged_attn_prefill(*args(d=bad)) == -1
-    # the no-alloc entry rejects, before any device call, a layout whose split-KV
-    # partials exceed its fixed 64 MiB scratch (64K context, 64 q heads)
-    d2 = hk.dims(1, 64, 8, 128, 16, 2)
-    m2 = hk.HostMeta([0, 2], [0, 65536], [65536, 4096], [0] * 8, [0] * 8, [-1] * 16)
-    s2 = hk.segkv_plan_sizes(d2, m2)
-    assert s2["attn_workspace_bytes"] > 64 << 20
-    rc = lib.segpaged_attn_prefill_noalloc(ctypes.byref(d2), ctypes.byref(m2.struct()), 16, 16, 16, 10, 16, 16,
-                                           16, s2["plan_bytes"], 0.125, 16, None, None)
-    assert rc == -5 and b"no-alloc" in lib.segkv_last_error()
-    nargs = args(q=8)[:-3] + [None]
-    assert lib.segpaged_attn_prefill_noalloc(*nargs) == -4
+    # the no-alloc entry validates like the workspace entry, before any device call
+    nargs = lambda **kw: args(**kw)[:-3] + [None]
+    assert lib.segpaged_attn_prefill_noalloc(*nargs(q=None)) == -1
+    assert lib.segpaged_attn_prefill_noalloc(*nargs(q=8)) == -4
+    assert lib.segpaged_attn_prefill_noalloc(*nargs(plan_bytes=8)) == -5
     # build_pages: capacity below the exact table size
     dm = hk.Meta(16, 16, 16, 16, 16, 16)
     rc = lib.segkv_build_pages(ctypes.byref(d), ctypes.byref(ms), ctypes.byref(dm), 16, 16, 16, 16, 16, 16,

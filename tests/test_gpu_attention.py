@@ -236,6 +236,29 @@ def test_full_size_zero_q_counts_visible_keys(name):
             assert np.all(np.abs(got - np.log(np.repeat(n, G))) <= 1e-5 * np.log(np.repeat(n, G)) + 1e-6), row
 
 
+def test_items_longer_than_the_table_ring():
+    """4096 query rows, 64 q heads over 8 global kv heads, 36,864 keys: 1024
+    m-tiles, so the plan splits none and each item walks its whole m-tile,
+    up to 576 key tiles, refilling its 256-tile LDS table ring twice. Q = 0
+    probes every row (exp(LSE) = position + 1); the real Q is compared with
+    the oracle on rows spread over the m-tiles."""
+    w = workloads.make_custom("ring_576", Hq=64, Hkv=8, D=128, theta=1e6,
+                              seg_lens_per_req=[[16384, 16384, 4096]], orig_starts_per_req=[[0, 0, None]],
+                              classes=[G_] * 8, windows=[0] * 8)
+    print(f"case {w.name}: items of up to 576 tiles", flush=True)
+    layer, dev = build(w)
+    assert layer.sizes["attn_workspace_bytes"] == 0  # no item is split
+    rows = list(range(0, 4096, 61)) + [4095]
+    out, lse = layer.attention(dev.q, dev.k_work, dev.v_work)
+    torch.cuda.synchronize()
+    O, L = oracle.attention(w, rows=rows)
+    assert_attn_close(bits(out), lse.cpu().numpy(), O, L, rows=rows, name=w.name)
+    _, lse0 = layer.attention(torch.zeros_like(dev.q), dev.k_work, dev.v_work)
+    torch.cuda.synchronize()
+    pos = 32768 + np.arange(4096, dtype=np.float64)
+    assert np.all(np.abs(lse0.cpu().numpy().astype(np.float64) - np.log(pos + 1)[:, None]) <= 1e-5 * np.log(pos + 1)[:, None])
+
+
 @pytest.mark.parametrize("make", [workloads.tiny, workloads.mistral_32k], ids=["tiny_224", "mistral7b_32k"])
 def test_relocate_then_attend(make):
     """BUILDSTATE relocation (head-aware moves) followed by EXECUTE attention;
