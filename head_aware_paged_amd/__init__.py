@@ -61,11 +61,14 @@ class Sizes(ctypes.Structure):
 _lib = None
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libsegkv.so (built in-tree by ``__graft_entry__.build()``)."""
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libsegkv.so (built in-tree by ``__graft_entry__.build()``; the
+    SEGKV_LIB environment variable names another build of the same library,
+    such as the sanitizer build of its host code)."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("SEGKV_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise ImportError(f"libsegkv.so not found at {path}; build it with __graft_entry__.build()")
     lib = ctypes.CDLL(path)
