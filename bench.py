@@ -109,24 +109,89 @@ def source_hash(names):
 
 def cpu_baseline(w, pairs_per_row, min_seconds):
     """The fp64 oracle on the same workload: whole passes over every query row
-    (all heads) until at least min_seconds of host time have been spent."""
+    (all heads) until at least min_seconds of host time have been spent, with
+    the BLAS pool set to the cores this process may run on (capped by
+    OMP_NUM_THREADS, the job's share of the host, when that is set)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+    from threadpoolctl import threadpool_info, threadpool_limits
+    affinity = len(os.sched_getaffinity(0))
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(affinity, share) if share > 0 else affinity
+    blas = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+    vendor = ",".join(sorted({f"{d.get('internal_api')} {d.get('version')}" for d in blas})) or "unknown"
     passes, dt = 0, 0.0
-    while passes == 0 or dt < min_seconds:
-        t0 = time.perf_counter()
-        oracle.attention(w)
-        dt += time.perf_counter() - t0
-        passes += 1
+    with threadpool_limits(limits=threads, user_api="blas"):
+        used = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+        while passes == 0 or dt < min_seconds:
+            t0 = time.perf_counter()
+            oracle.attention(w)
+            dt += time.perf_counter() - t0
+            passes += 1
     flops = 4.0 * w.head_dim * float(pairs_per_row.sum()) * passes
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(used), "affinity_cores": affinity,
+            "blas": vendor, "kind": "oracle",
             "sample": f"fp64 oracle attention (explicit per-head masks) over all {w.total_q_rows} query rows x "
                       f"{w.num_q_heads} q heads of {w.name}, {passes} pass(es): {flops / 1e9:.1f} GFLOP of "
                       f"visible pairs in {dt:.1f} s"}
+
+
+def relocation_bandwidth(w, dev, i32, k_only=False, reps=20):
+    """rope_relocate on a workload's structure: every reused page (full) and the
+    head-aware move list, K+V (and K alone if k_only), each timed per call with
+    HIP events on the launching stream over rotating sets of pools that
+    together exceed 3x the 256 MB Infinity Cache, so every call reads and
+    writes HBM. Pools hold N(0, 1) bf16 drawn on the device."""
+    import numpy as np
+    import torch
+    from head_aware_paged_amd import rope_relocate
+    from head_aware_paged_amd.session import SegPagedLayer
+    Hkv, D = w.num_kv_heads, w.head_dim
+    src, dst, dl = [], [], []
+    for r in range(w.num_requests):
+        for s in w.segments_of(r)[:-1]:
+            for h in range(Hkv):
+                a, b = w.cache_page_indptr[s * Hkv + h], w.cache_page_indptr[s * Hkv + h + 1]
+                c, d = w.seg_page_indptr[s * Hkv + h], w.seg_page_indptr[s * Hkv + h + 1]
+                src.extend(w.cache_pages[a:b])
+                dst.extend(w.seg_pages[c:d])
+                dl.extend([int(w.seg_start[s] - w.seg_orig_start[s])] * (b - a))
+    layer = SegPagedLayer(w.num_q_heads, Hkv, D, w.seg_indptr, w.seg_start, w.seg_len, w.head_class, w.window,
+                          w.retr_seg, page_size=16, device=dev)
+    layer.build_pages(i32(w.seg_page_indptr), i32(w.seg_pages), i32(w.cache_page_indptr), i32(w.cache_pages),
+                      i32(w.seg_orig_start))
+    lists = {"full": (i32(src), i32(dst), i32(dl), len(src)),
+             "head_aware": (layer.move_src, layer.move_dst, layer.move_delta, layer.num_moves)}
+    n_cache, n_work = int(w.cache_page_indptr[-1]), int(w.seg_page_indptr[-1])
+    set_bytes = 2 * (n_cache + n_work) * 16 * D * 2
+    nsets = max(3, math.ceil(3 * 256e6 / set_bytes))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+
+    def pool(n, shape):
+        return torch.randn(n, *shape, generator=gen, device=dev).to(torch.bfloat16)
+    sets = [(pool(n_cache, (16, D)), pool(n_cache, (D, 16)), pool(n_work, (16, D)), pool(n_work, (D, 16)))
+            for _ in range(nsets)]
+    out = {}
+    for lname, (s_, d_, dl_, n) in lists.items():
+        for kv in ((True, False) if (k_only and lname == "full") else (True,)):
+            tot = 0.0
+            for rep in range(reps + nsets):
+                kc, vc, kw, vw = sets[rep % nsets]
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                rope_relocate(kc, kw, vc if kv else None, vw if kv else None, s_, d_, dl_, n, 16, D, w.rope_theta)
+                e1.record()
+                torch.cuda.synchronize()
+                if rep >= nsets:
+                    tot += e0.elapsed_time(e1)
+            t = tot / reps
+            nbytes = 2.0 * n * 16 * D * 2 * (2 if kv else 1)
+            out[f"{lname}_{'kv' if kv else 'k'}"] = {
+                "moves": n, "bytes": nbytes, "us": t * 1e3, "GB/s": nbytes / (t * 1e-3) / 1e9,
+                "pct_hbm_peak": 100.0 * nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    out["rotating_sets"] = f"{nsets} x {set_bytes / 1e6:.0f} MB"
+    del sets, layer
+    return out
 
 
 def main():
@@ -294,7 +359,10 @@ def main():
         "breakdown_us": {"build_pages": t_pages * 1e3, "rope_relocate_head_aware": t_reloc * 1e3,
                          "segpaged_attn_prefill": t_attn * 1e3, "token_importance_topk": t_imp * 1e3},
         "attention": {"tflops": attn_tflops, "pct_bf16_peak": 100.0 * attn_tflops / PEAK_BF16_TFLOPS},
-        "relocate_head_aware": {"moves": layer.num_moves, "GB/s": ha_bytes / (t_reloc * 1e-3) / 1e9},
+        "relocate_head_aware": {"moves": layer.num_moves, "us_in_step": t_reloc * 1e3,
+                                "GB/s_in_step": ha_bytes / (t_reloc * 1e-3) / 1e9,
+                                "note": "in_step: 10 calls per graph on the same 41 MB, cache-resident; "
+                                        "hbm: per call on rotating buffer sets"},
     }
     traffic = profile_traffic("attn_main_mistral7b_32k", source_hash(["attention.hip", "plan.h", "common.h"]))
     result["roofline"] = {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -303,39 +371,11 @@ def main():
                           "algorithmic": f"{flops / 1e9:.3f} GFLOP per launch = 4*D*visible pairs"}
 
     if not args.skip_extras:
-        # full relocation bandwidth (every reused page, K+V), three rotating buffer sets > 2x Infinity Cache
-        from head_aware_paged_amd import rope_relocate
-        Hkv = w.num_kv_heads
-        src, dst, dl = [], [], []
-        for s in w.segments_of(0)[:-1]:
-            for h in range(Hkv):
-                a, b = w.cache_page_indptr[s * Hkv + h], w.cache_page_indptr[s * Hkv + h + 1]
-                c, d = w.seg_page_indptr[s * Hkv + h], w.seg_page_indptr[s * Hkv + h + 1]
-                src.extend(w.cache_pages[a:b]); dst.extend(w.seg_pages[c:d])
-                dl.extend([int(w.seg_start[s] - w.seg_orig_start[s])] * (b - a))
-        src_t, dst_t, dl_t = i32(src), i32(dst), i32(dl)
-        n_mv = len(src)
-        sets = [(k_cache, v_cache, k_work, v_work)] + [
-            (k_cache.clone(), v_cache.clone(), k_work.clone(), v_work.clone()) for _ in range(2)]
-        reps = 30
-        for kv in (True, False):
-            tot = 0.0
-            for rep in range(reps + 3):
-                kc, vc, kw, vw = sets[rep % 3]
-                a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a0.record()
-                rope_relocate(kc, kw, vc if kv else None, vw if kv else None, src_t, dst_t, dl_t, n_mv, 16, D,
-                              w.rope_theta)
-                a1.record()
-                torch.cuda.synchronize()
-                if rep >= 3:
-                    tot += a0.elapsed_time(a1)
-            t = tot / reps
-            nbytes = 2.0 * n_mv * 16 * D * 2 * (2 if kv else 1)
-            result["relocate_full_kv" if kv else "relocate_full_k"] = {
-                "moves": n_mv, "bytes": nbytes, "us": t * 1e3, "GB/s": nbytes / (t * 1e-3) / 1e9,
-                "pct_hbm_peak": 100.0 * nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBPS}
-        # plain device copy of 256 MiB, for calibration
+        # relocation bandwidth on HBM (rotating buffer sets) for the three attention layouts
+        result["relocate"] = {"mistral7b_32k": relocation_bandwidth(w, dev, i32, k_only=True)}
+        for wname, make in (("qwen3_32b_varlen", workloads.qwen_varlen), ("long_64k", workloads.long_64k)):
+            result["relocate"][wname] = relocation_bandwidth(make(with_data=False), dev, i32)
+        # plain device copy of 256 MiB (torch), for calibration
         xa = torch.empty(128 << 20, dtype=torch.bfloat16, device=dev)
         xb = torch.empty_like(xa)
         for _ in range(3):
@@ -347,9 +387,14 @@ def main():
         a1.record()
         torch.cuda.synchronize()
         result["copy_256MiB_GB/s"] = 2.0 * xa.numel() * 2 * 10 / (a0.elapsed_time(a1) * 1e-3) / 1e9
-        del xa, xb, sets
-        log(f"relocate full K+V {result['relocate_full_kv']['GB/s']:.0f} GB/s, "
-            f"K only {result['relocate_full_k']['GB/s']:.0f} GB/s, copy {result['copy_256MiB_GB/s']:.0f} GB/s")
+        del xa, xb
+        rl = result["relocate"]
+        result["relocate_head_aware"]["GB/s_hbm"] = rl["mistral7b_32k"]["head_aware_kv"]["GB/s"]
+        result["relocate_head_aware"]["us_hbm"] = rl["mistral7b_32k"]["head_aware_kv"]["us"]
+        for wname, r_ in rl.items():
+            log(f"relocate {wname}: full K+V {r_['full_kv']['GB/s']:.0f} GB/s, head-aware K+V "
+                f"{r_['head_aware_kv']['GB/s']:.0f} GB/s ({r_['head_aware_kv']['us']:.1f} us)")
+        log(f"copy {result['copy_256MiB_GB/s']:.0f} GB/s")
 
         # decode step of the same layer: one new row per request over the same page tables
         dq, dk, dv = (bf16(x) for x in workloads.decode_inputs(w, seed=0))

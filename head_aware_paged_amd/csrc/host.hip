@@ -165,9 +165,7 @@ static int choose_chunk_tiles(const std::vector<int>& tiles, int slots) {
   return best_S;
 }
 
-int32_t compute_host_plan(const segkv_dims* d, const segkv_meta* m, HostPlan* out) {
-  int32_t st = validate_layout(d, m);
-  if (st != SEGKV_OK) return st;
+static int32_t plan_layout_uncached(const segkv_dims* d, const segkv_meta* m, HostPlan* out) {
   HostPlan p;
   const int R = d->num_requests, Hkv = d->num_kv_heads;
   const int G = d->num_q_heads / Hkv;
@@ -223,6 +221,47 @@ int32_t compute_host_plan(const segkv_dims* d, const segkv_meta* m, HostPlan* ou
   const PlanLayout L = host_plan_layout(*d, p);
   p.plan_bytes = L.total;
   p.workspace_bytes = (size_t)p.n_partials * partial_slot_bytes(d->head_dim);
+  *out = p;
+  return SEGKV_OK;
+}
+
+// The host plan of a layout, cached: every entry point of a layer (page build,
+// attention, importance) plans the same layout, once per call, so the last few
+// layouts' plans are kept, keyed by the complete layout (dims, every metadata
+// array and the slot count).
+int32_t compute_host_plan(const segkv_dims* d, const segkv_meta* m, HostPlan* out) {
+  int32_t st = validate_layout(d, m);
+  if (st != SEGKV_OK) return st;
+  const int R = d->num_requests, S = d->num_segments, RH = R * d->num_kv_heads;
+  std::vector<int32_t> key = {d->num_requests, d->num_q_heads, d->num_kv_heads, d->head_dim, d->page_size,
+                              d->num_segments, attention_slots()};
+  key.reserve(key.size() + (R + 1) + 2 * S + 4 * RH);
+  key.insert(key.end(), m->seg_indptr, m->seg_indptr + R + 1);
+  key.insert(key.end(), m->seg_start, m->seg_start + S);
+  key.insert(key.end(), m->seg_len, m->seg_len + S);
+  for (int k = 0; k < RH; ++k) key.push_back(m->head_class[k]);
+  key.insert(key.end(), m->window, m->window + RH);
+  key.insert(key.end(), m->retr_seg, m->retr_seg + 2 * RH);
+  static std::mutex mu;
+  static std::vector<std::pair<std::vector<int32_t>, HostPlan>> cache;  // most recent last
+  constexpr size_t kCacheLayouts = 16;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (size_t i = 0; i < cache.size(); ++i)
+      if (cache[i].first == key) {
+        *out = cache[i].second;
+        if (i + 1 != cache.size()) std::rotate(cache.begin() + i, cache.begin() + i + 1, cache.end());
+        return SEGKV_OK;
+      }
+  }
+  HostPlan p;
+  st = plan_layout_uncached(d, m, &p);
+  if (st != SEGKV_OK) return st;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache.size() == kCacheLayouts) cache.erase(cache.begin());
+    cache.emplace_back(std::move(key), p);
+  }
   *out = p;
   return SEGKV_OK;
 }

@@ -86,7 +86,9 @@ __global__ __launch_bounds__(kRelocThreads) void relocate_kernel(
     const int b = e / kHalf, j = e % kHalf;
     float sn = 0.f, cn = 1.f;
     if (s_ok[b]) {
-      // angle in fp64, reduced to [-pi, pi] in fp64 (2 pi in two parts), cos/sin in fp32
+      // angle in fp64, reduced to [-pi, pi] in fp64 by Cody-Waite reduction
+      // (x - n C1 - n C2 with 2 pi = C1 + C2, C1 the fp64 value of 2 pi and C2
+      // its remainder), then cos/sin in fp32
       const double ang = (double)s_delta[b] * inv_freq[j];
       const double n = rint(ang * 0.15915494309189535);
       sincosf((float)fma(-n, 2.4492935982947064e-16, fma(-n, 6.283185307179586, ang)), &sn, &cn);
