@@ -273,9 +273,10 @@ __global__ __launch_bounds__(256) void importance_reduce_kernel(const char* __re
 
 // ---- top-k: radix select on order-preserving integer keys ----
 //
-// One 1024-thread work-group selects the top k of one score vector. Wave w
-// owns the contiguous key range [256 S w, 256 S (w + 1)); inside it, sub-block
-// u holds keys 256 u + 4 lane + e (e < 4), kept in registers for every pass.
+// One 1024-thread work-group selects the top k of one score vector (one
+// work-group per request, all in one launch). Wave w owns the contiguous key
+// range [256 S w, 256 S (w + 1)); inside it, sub-block u holds keys
+// 256 u + 4 lane + e (e < 4), kept in registers for every pass.
 // Up to four 8-bit digit passes find the k-th largest key. Each pass counts
 // the candidates' digits in 64 lane-private LDS histograms (bin b of lane l at
 // 64 b + l, so a wave's increments never share a bank or an address). Every
@@ -295,6 +296,14 @@ constexpr int kTopkSegSub = 9;       // up to 9 sub-blocks per wave, every wave'
 constexpr int kTopkLdsWords = kTopkWaves * kTopkSub * kTopkSegSub + 64;  // >= both histogram buffers
 constexpr int kTopkStageMax = kTopkLdsWords - 64;  // staged output indices; the last 64 words take unselected writes
 static_assert(kTopkStageMax >= 2 * kTopkHist, "the LDS array must hold both histogram buffers");
+constexpr int kTopkMaxJobs = 64;  // score vectors per launch
+
+// The score vectors of one launch: vector j has n[j] keys at scores + off[j]
+// and writes its k[j] indices at idx + koff[j].
+struct TopkJobs {
+  int64_t off[kTopkMaxJobs], koff[kTopkMaxJobs];
+  int n[kTopkMaxJobs], k[kTopkMaxJobs];
+};
 
 // fp32 bit pattern -> unsigned integer of the same order (-0 ranks as +0)
 __device__ __forceinline__ uint32_t ordered_bits(uint32_t b) {
@@ -340,12 +349,17 @@ __device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
 }
 
 template <int S>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
-                                                            int32_t* __restrict__ idx_out, int n, int k, int ns_rt) {
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores_all,
+                                                            int32_t* __restrict__ idx_all, const TopkJobs jobs,
+                                                            int ns_rt) {
   __shared__ uint32_t hist[kTopkLdsWords];  // two histogram buffers; afterwards the staged output
   __shared__ u32x4 s_bins[64];              // bin totals of the current pass
   __shared__ int s_tot[kTopkWaves][2];
   constexpr int SR = S > 0 ? S : 1;
+  const int n = jobs.n[blockIdx.x], k = jobs.k[blockIdx.x];
+  if (k <= 0) return;
+  const float* scores = scores_all + jobs.off[blockIdx.x];
+  int32_t* idx_out = idx_all + jobs.koff[blockIdx.x];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ns = S > 0 ? S : ns_rt;
   const int base = wave * ns * kTopkSub + 4 * lane;
@@ -594,12 +608,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
 }
 #pragma clang diagnostic pop
 
-int32_t launch_topk(const float* scores, int32_t* idx, int n, int k, hipStream_t s) {
-  if (k <= 0) return SEGKV_OK;
-  if (n > (1 << 30)) return fail(SEGKV_ERR_UNSUPPORTED, "top-k vectors are limited to 2^30 keys");
-  const int ns = cdiv(n, kTopkWaves * kTopkSub);  // sub-blocks per wave
-  const dim3 g(1), b(kTopkThreads);
-#define SEGKV_TOPK(SV) topk_kernel<SV><<<g, b, 0, s>>>(scores, idx, n, k, ns)
+// One launch selects up to kTopkMaxJobs vectors, one work-group each; the
+// register-resident sub-block count follows the longest vector.
+int32_t launch_topk_jobs(const float* scores, int32_t* idx, const TopkJobs& jobs, int n_jobs, hipStream_t s) {
+  int max_n = 0;
+  for (int j = 0; j < n_jobs; ++j) {
+    if (jobs.n[j] > (1 << 30)) return fail(SEGKV_ERR_UNSUPPORTED, "top-k vectors are limited to 2^30 keys");
+    max_n = imax(max_n, jobs.n[j]);
+  }
+  const int ns = imax(1, cdiv(max_n, kTopkWaves * kTopkSub));  // sub-blocks per wave
+  const dim3 g(n_jobs), b(kTopkThreads);
+#define SEGKV_TOPK(SV) topk_kernel<SV><<<g, b, 0, s>>>(scores, idx, jobs, ns)
   switch (ns <= kTopkMaxRegSub ? ns : 0) {
     case 1: SEGKV_TOPK(1); break;
     case 2: SEGKV_TOPK(2); break;
@@ -703,15 +722,25 @@ extern "C" int32_t token_importance_topk(const segkv_dims* dims, const segkv_met
                                                                       hp.total_keys, hp.key_blocks);
   SEGKV_LAUNCH_CHECK();
   if (topk_idx_dev == nullptr) return SEGKV_OK;
-  // one selection per request on the same stream (host knows every offset)
+  // the requests' selections, kTopkMaxJobs per launch (host knows every offset)
+  TopkJobs jobs;
+  int nj = 0;
   int64_t off = 0, koff = 0;
   for (int r = 0; r < R; ++r) {
     const int sq = meta_host->seg_indptr[r + 1] - 1;
     const int lk = meta_host->seg_start[sq] + meta_host->seg_len[sq];
-    st = launch_topk(importance_dev + off, topk_idx_dev + koff, lk, k_host[r], s);
-    if (st != SEGKV_OK) return st;
+    jobs.off[nj] = off;
+    jobs.koff[nj] = koff;
+    jobs.n[nj] = lk;
+    jobs.k[nj] = k_host[r];
+    ++nj;
     off += lk;
     koff += k_host[r];
+    if (nj == kTopkMaxJobs || r == R - 1) {
+      st = launch_topk_jobs(importance_dev, topk_idx_dev, jobs, nj, s);
+      if (st != SEGKV_OK) return st;
+      nj = 0;
+    }
   }
   return SEGKV_OK;
 }
@@ -722,5 +751,10 @@ extern "C" int32_t segkv_topk_select(const float* scores_dev, int32_t n, int32_t
   if (n < 0 || k < 0 || k > n) return fail(SEGKV_ERR_INVALID_ARG, "need 0 <= k <= n");
   if (k == 0) return SEGKV_OK;
   if (!scores_dev || !idx_dev) return fail(SEGKV_ERR_INVALID_ARG, "a required pointer is NULL");
-  return launch_topk(scores_dev, idx_dev, n, k, static_cast<hipStream_t>(stream));
+  TopkJobs jobs;
+  jobs.off[0] = 0;
+  jobs.koff[0] = 0;
+  jobs.n[0] = n;
+  jobs.k[0] = k;
+  return launch_topk_jobs(scores_dev, idx_dev, jobs, 1, static_cast<hipStream_t>(stream));
 }
