@@ -16,8 +16,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsegkv.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libsegkv_debug.so")
 
 SEGKV_OK = 0
+SEGKV_ERR_DEVICE_CHECK = -7
 GLOBAL, LOCAL, RETRIEVAL, DENSE = 0, 1, 2, 3
 
 EXPORTS = [
@@ -61,17 +63,8 @@ class Sizes(ctypes.Structure):
 _lib = None
 
 
-def load(path: Optional[str] = None) -> ctypes.CDLL:
-    """Load libsegkv.so (built in-tree by ``__graft_entry__.build()``; the
-    SEGKV_LIB environment variable names another build of the same library,
-    such as the sanitizer build of its host code)."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    path = path or os.environ.get("SEGKV_LIB") or LIB_PATH
-    if not os.path.exists(path):
-        raise ImportError(f"libsegkv.so not found at {path}; build it with __graft_entry__.build()")
-    lib = ctypes.CDLL(path)
+def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Declare every entry point's argument and result types."""
     P, I32, I64, F32, F64, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                  ctypes.c_double, ctypes.c_size_t)
     sig = {
@@ -100,8 +93,30 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
-    _lib = lib
     return lib
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libsegkv.so (built in-tree by ``__graft_entry__.build()``; the
+    SEGKV_LIB environment variable names another build of the same library,
+    such as the sanitizer build of its host code)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or os.environ.get("SEGKV_LIB") or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"libsegkv.so not found at {path}; build it with __graft_entry__.build()")
+    _lib = _configure(ctypes.CDLL(path))
+    return _lib
+
+
+def load_debug() -> ctypes.CDLL:
+    """The SEGKV_DEBUG build (device-side bounds checks, synchronous entry
+    points) as a separate library handle; the binding functions keep using
+    load()."""
+    if not os.path.exists(DEBUG_LIB_PATH):
+        raise ImportError(f"libsegkv_debug.so not found at {DEBUG_LIB_PATH}; build it with __graft_entry__.build()")
+    return _configure(ctypes.CDLL(DEBUG_LIB_PATH))
 
 
 def _check(fn: str, code: int):

@@ -7,6 +7,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsegkv.so")
+DEBUG_LIB = os.path.join(HERE, "libsegkv_debug.so")  # SEGKV_DEBUG: device-side bounds checks
 SOURCES = ["host.hip", "pages.hip", "relocate.hip", "attention.hip", "decode.hip", "importance.hip", "ffn.hip",
            "dense.hip"]
 
@@ -40,15 +41,16 @@ def asan_runtime() -> str:
 DEVICE_FLAGS = {}
 
 
-def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, sanitize: bool = False, debug: bool = False) -> str:
     """Compile every HIP source for gfx950 (one object each, in parallel) and
     link them into one shared library; returns its path. sanitize=True builds
-    the host code with ASan/UBSan (at -O1)."""
+    the host code with ASan/UBSan (at -O1); debug=True defines SEGKV_DEBUG
+    (device-side bounds checks reported as SEGKV_ERR_DEVICE_CHECK)."""
     import concurrent.futures
     import tempfile
     base = [hipcc(), "--offload-arch=gfx950", "-O1" if sanitize else "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-result"] + \
-        (HOST_SANITIZE + ["-g"] if sanitize else [])
+        (HOST_SANITIZE + ["-g"] if sanitize else []) + (["-DSEGKV_DEBUG"] if debug else [])
     tmpdir = tempfile.mkdtemp(prefix="segkv_build_")
 
     def compile_one(src):
@@ -82,3 +84,4 @@ def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build(out=DEBUG_LIB, debug=True))

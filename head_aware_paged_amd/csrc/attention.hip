@@ -30,6 +30,8 @@
 namespace segkv {
 namespace {
 
+SEGKV_DEVICE_FLAG(g_attn_check);  // bit 1: table page id outside the pool; bit 2: page position not a page start
+
 constexpr int kAttnWaves = 8;                   // waves per attention work-group
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kCombineThreads = 256;
@@ -194,6 +196,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
     if (e < mt.e_end) {
       pid = a.page_ids[e];
       ps = a.page_pos[e];
+      SEGKV_DCHECK(g_attn_check, pid >= 0 && pid < a.pool_pages, 1);
+      SEGKV_DCHECK(g_attn_check, ps >= 0 && ps % kPage == 0, 2);
       if (pid < 0 || pid >= a.pool_pages) {
         pid = -1;
         ps = INT_MAX;
@@ -775,6 +779,7 @@ int32_t attn_prefill(const segkv_dims* dims, const segkv_meta* meta_host, const 
     if (hp.n_split > 0) attn_combine_kernel<64><<<dim3(hp.n_split, kMRows * 16 / kCombineThreads), kCombineThreads, 0, s>>>(a);
   }
   SEGKV_LAUNCH_CHECK();
+  SEGKV_DEVICE_CHECK(g_attn_check, s, "segpaged_attn_prefill: a page-table entry is out of range");
   return SEGKV_OK;
 }
 }  // namespace

@@ -24,6 +24,40 @@ void clear_error();
 
 #define SEGKV_LAUNCH_CHECK() SEGKV_HIP_CHECK(hipGetLastError())
 
+// Debug builds (compiled with SEGKV_DEBUG): kernels check the page ids and page
+// positions they read and OR a bit into a device flag of their source file
+// when one is out of range (release builds treat such a page as missing, or
+// skip such a move, and check nothing). After its launches the entry point
+// waits for the stream, reads the flag back, clears it, and returns
+// SEGKV_ERR_DEVICE_CHECK if any bit was set. The wait makes debug builds
+// synchronous, so they are for testing, not for graph capture.
+#ifdef SEGKV_DEBUG
+#define SEGKV_DEVICE_FLAG(name) static __device__ int name = 0
+#define SEGKV_DCHECK(flag, cond, bit)        \
+  do {                                       \
+    if (!(cond)) atomicOr(&(flag), (bit));   \
+  } while (0)
+#define SEGKV_DEVICE_CHECK(flag, stream, what)                                                          \
+  do {                                                                                                \
+    SEGKV_HIP_CHECK(hipStreamSynchronize(stream));                                                    \
+    int v_ = 0;                                                                                       \
+    SEGKV_HIP_CHECK(hipMemcpyFromSymbol(&v_, HIP_SYMBOL(flag), sizeof(int), 0, hipMemcpyDeviceToHost)); \
+    if (v_ != 0) {                                                                                    \
+      const int z_ = 0;                                                                               \
+      SEGKV_HIP_CHECK(hipMemcpyToSymbol(HIP_SYMBOL(flag), &z_, sizeof(int), 0, hipMemcpyHostToDevice)); \
+      return ::segkv::fail(SEGKV_ERR_DEVICE_CHECK, std::string(what) + " (check bits " + std::to_string(v_) + ")"); \
+    }                                                                                                 \
+  } while (0)
+#else
+#define SEGKV_DEVICE_FLAG(name) static_assert(true, "")
+#define SEGKV_DCHECK(flag, cond, bit) \
+  do {                                \
+  } while (0)
+#define SEGKV_DEVICE_CHECK(flag, stream, what) \
+  do {                                         \
+  } while (0)
+#endif
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ---- host-side layout helpers ----

@@ -19,6 +19,8 @@
 namespace segkv {
 namespace {
 
+SEGKV_DEVICE_FLAG(g_dec_check);  // bit 1: a table page id outside the pool
+
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kDecPagesPerWave = 2;
@@ -99,6 +101,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_main_kernel(DecArgs a) {
     const int ec = have[p] ? e : e0;
     int pid = a.page_ids[ec];
     pos0[p] = a.page_pos[ec];
+    SEGKV_DCHECK(g_dec_check, !have[p] || (pid >= 0 && pid < a.pool_pages), 1);
     if (pid < 0 || pid >= a.pool_pages) {
       have[p] = false;
       pid = 0;
@@ -378,5 +381,6 @@ extern "C" int32_t segpaged_attn_decode(const segkv_dims* dims, const segkv_meta
   else
     decode_combine_kernel<64><<<dim3(a.R * a.Hq, 64 / kDecCombDims), kDecCombThreads, 0, s>>>(a);
   SEGKV_LAUNCH_CHECK();
+  SEGKV_DEVICE_CHECK(g_dec_check, s, "segpaged_attn_decode: a page-table entry is out of range");
   return SEGKV_OK;
 }

@@ -279,6 +279,7 @@ extern "C" const char* segkv_status_string(int32_t s) {
     case SEGKV_ERR_ALIGNMENT: return "SEGKV_ERR_ALIGNMENT";
     case SEGKV_ERR_WORKSPACE: return "SEGKV_ERR_WORKSPACE";
     case SEGKV_ERR_HIP: return "SEGKV_ERR_HIP";
+    case SEGKV_ERR_DEVICE_CHECK: return "SEGKV_ERR_DEVICE_CHECK";
     default: return "SEGKV_ERR_UNKNOWN";
   }
 }

@@ -22,6 +22,8 @@
 namespace segkv {
 namespace {
 
+SEGKV_DEVICE_FLAG(g_imp_check);  // bit 1: a table page id outside the pool
+
 constexpr int kImpThreads = 256;
 constexpr int kImpWaves = kImpThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -99,7 +101,10 @@ __global__ __launch_bounds__(kImpThreads, 3) void importance_kernel(ImpArgs a) {
   for (int u = 0; u < kTilePages; ++u) pid[u] = a.page_ids[imax(ent[u], 0)];
   const int pool_pages = a.pool_pages < INT32_MAX ? (int)a.pool_pages : INT32_MAX;
 #pragma unroll
-  for (int u = 0; u < kTilePages; ++u) pid[u] = ent[u] < 0 || pid[u] < 0 || pid[u] >= pool_pages ? -1 : pid[u];
+  for (int u = 0; u < kTilePages; ++u) {
+    SEGKV_DCHECK(g_imp_check, ent[u] < 0 || (pid[u] >= 0 && pid[u] < pool_pages), 1);
+    pid[u] = ent[u] < 0 || pid[u] < 0 || pid[u] >= pool_pages ? -1 : pid[u];
+  }
   // log2-scaled LSE of the last n rows of this head's G query heads, [g][t]
   // with t < NP (rows past n repeat row n - 1)
   const int n_lse = a.G * NP;
@@ -721,6 +726,7 @@ extern "C" int32_t token_importance_topk(const segkv_dims* dims, const segkv_met
   importance_reduce_kernel<<<dim3(cdiv(max_lk, 256), R), 256, 0, s>>>(a.plan, a.L, a.partial, importance_dev,
                                                                       hp.total_keys, hp.key_blocks);
   SEGKV_LAUNCH_CHECK();
+  SEGKV_DEVICE_CHECK(g_imp_check, s, "token_importance_topk: a page-table entry is out of range");
   if (topk_idx_dev == nullptr) return SEGKV_OK;
   // the requests' selections, kTopkMaxJobs per launch (host knows every offset)
   TopkJobs jobs;

@@ -19,6 +19,8 @@
 namespace segkv {
 namespace {
 
+SEGKV_DEVICE_FLAG(g_reloc_check);  // bit 1: a move's source or destination page outside its pool
+
 constexpr int kRelocThreads = 128;
 template <int D>
 constexpr int moves_per_batch() { return D == 128 ? 1 : 2; }
@@ -52,6 +54,7 @@ __global__ __launch_bounds__(kRelocThreads) void relocate_kernel(
       d = dst_page[m];
       dl = delta[m];
       ok = (s >= 0 && s < src_pages && d >= 0 && d < dst_pages) ? 1 : 0;
+      SEGKV_DCHECK(g_reloc_check, ok, 1);
     }
     s_src[tid] = s;
     s_dst[tid] = d;
@@ -172,5 +175,6 @@ extern "C" int32_t rope_relocate(const void* k_src, void* k_dst, const void* v_s
     relocate_kernel<64><<<grid, kRelocThreads, 0, s>>>(ks, kd, vs, vd, src_pool_pages, dst_pool_pages,
                                                        src_page_dev, dst_page_dev, delta_dev, n_moves, std::log2(rope_theta));
   SEGKV_LAUNCH_CHECK();
+  SEGKV_DEVICE_CHECK(g_reloc_check, s, "rope_relocate: a move's page id is outside its pool");
   return SEGKV_OK;
 }

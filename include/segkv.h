@@ -16,7 +16,14 @@
  *  - Arguments are validated on the host before anything is launched; a call
  *    that returns an error has enqueued no GPU work.
  *  - Device work is enqueued on `stream` (a hipStream_t; NULL is the null
- *    stream) and is asynchronous: no call synchronises the host.
+ *    stream) and is asynchronous: no call synchronises the host. The one
+ *    exception is the debug build (libsegkv_debug.so, compiled with
+ *    SEGKV_DEBUG): there rope_relocate, segpaged_attn_prefill (all forms),
+ *    segpaged_attn_decode and token_importance_topk check every page id they
+ *    read against the pool (and attention every table position against page
+ *    starts), wait for the stream after their launches, and return
+ *    SEGKV_ERR_DEVICE_CHECK if a check failed; the release build treats such
+ *    a page as missing (or skips such a move) without reporting it.
  *  - The caller owns and allocates every buffer. The library allocates no
  *    device memory and keeps no device state between calls; scratch space is
  *    passed in as `workspace`/`plan`.
@@ -46,6 +53,7 @@ extern "C" {
 #define SEGKV_ERR_ALIGNMENT (-4)     /* a device pointer is not 16-byte aligned */
 #define SEGKV_ERR_WORKSPACE (-5)     /* workspace/plan buffer too small */
 #define SEGKV_ERR_HIP (-6)           /* a HIP runtime call failed (no device, launch failure) */
+#define SEGKV_ERR_DEVICE_CHECK (-7)  /* debug builds only (SEGKV_DEBUG): a device-side bounds check failed */
 
 /* ---- head classes (RedKnot README, "About": global / local / retrieval / dense) ----
  * GLOBAL, DENSE : a query row at position i sees every key j <= i.

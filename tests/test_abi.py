@@ -34,7 +34,8 @@ def test_status_strings():
     lib = hk.load()
     assert lib.segkv_status_string(0) == b"SEGKV_OK"
     for code, name in [(-1, b"SEGKV_ERR_INVALID_ARG"), (-2, b"SEGKV_ERR_UNSUPPORTED"), (-3, b"SEGKV_ERR_CAPACITY"),
-                       (-4, b"SEGKV_ERR_ALIGNMENT"), (-5, b"SEGKV_ERR_WORKSPACE"), (-6, b"SEGKV_ERR_HIP")]:
+                       (-4, b"SEGKV_ERR_ALIGNMENT"), (-5, b"SEGKV_ERR_WORKSPACE"), (-6, b"SEGKV_ERR_HIP"),
+                       (-7, b"SEGKV_ERR_DEVICE_CHECK")]:
         assert lib.segkv_status_string(code) == name
 
 
