@@ -12,6 +12,7 @@
 // rows, B = token rows), so each lane ends up holding one token row and 4-wide
 // runs of output features, which the epilogues store as 8-byte bf16 groups.
 #include <climits>
+#include <mutex>
 
 #include "common.h"
 #include "plan.h"
@@ -199,6 +200,214 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(FfnArgs a) {
   }
 }
 
+// ---- large-tile projection for launches of at least one work-group per CU ----
+//
+// Same products and epilogues as ffn_gemm_kernel, with the operand traffic of
+// LDS cut in half: each wave computes (32 WA) x (32 WB) outputs (accumulators
+// beyond the 256 architectural VGPRs live in AGPRs, so one wave per SIMD),
+// the work-group (64 WA) weight rows x (64 WB) token rows. K goes in 32-deep
+// slices through a ring of kBigStages LDS stages, filled by buffer loads with
+// the LDS destination (no register staging), each slice issued
+// kBigStages - 1 slices ahead. A stage row is 32 bf16 = four 16-byte chunks;
+// chunk c of row r sits at slot c ^ ((r / 4) % 4), so the 16-byte operand
+// reads of 16 consecutive rows fall in distinct bank groups. Token rows that
+// do not exist (past k, or an out-of-range index) read as zeros through the
+// buffer's range check.
+constexpr int kBigBK = 32;        // reduction depth per slice
+constexpr int kBigStages = 4;     // LDS ring depth
+constexpr int kBigRowBytes = kBigBK * 2;
+constexpr int kBigRowsPerDma = 16;  // rows of one 1 KiB buffer-to-LDS instruction
+constexpr uint32_t kBigOob = 0x7FFFFFF0u;  // a source offset past every buffer: reads zeros
+// s_waitcnt immediate with lgkmcnt and expcnt at their maximum (not waited
+// for) and vmcnt n (gfx9 encoding: vmcnt low bits 3:0, high bits 15:14)
+constexpr int big_wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+__device__ __forceinline__ u32x4 big_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)), bytes, 0x00020000u};
+}
+__device__ __forceinline__ int big_swz(int row) { return (row >> 2) & 3; }
+
+// MODE kModeSwiglu: WA = 4; the A tile's 256 rows are gate rows f0 .. f0+63,
+// up rows f0 .. f0+63, gate rows f0+64 .., up rows f0+64 .. (64-row groups),
+// so wave wa holds gate blocks 0, 1 and the matching up blocks 2, 3 of
+// features f0 + 64 wa ... The work-group covers 128 features.
+template <int MODE, int WA, int WB>
+__global__ __launch_bounds__(kFfnThreads, 1) void ffn_big_kernel(FfnArgs a, uint32_t a_bytes, uint32_t x_bytes) {
+  constexpr int TA = 64 * WA, TB = 64 * WB;
+  constexpr int IA = TA / kBigRowsPerDma / 4, IB = TB / kBigRowsPerDma / 4;  // DMA instructions per wave and slice
+  constexpr int STAGE = (TA + TB) * kBigRowBytes;
+  constexpr int KSTEPS = kBigBK / 16;
+  static_assert(MODE != kModeSwiglu || WA == 4, "SwiGLU tile pairs gate and up blocks");
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int lrow = lane & 31, lg = lane >> 5;
+  const int wa = wave & 1, wb = wave >> 1;
+  const int f0 = blockIdx.x * (MODE == kModeSwiglu ? 128 : TA);  // first output feature
+  const int m0 = blockIdx.y * TB;                                 // first token row
+  const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+  const u32x4 rx = big_rsrc(a.x, x_bytes);
+  // this wave's DMA rows: instruction i covers stage rows (wave + 4 i) * 16 ..
+  u32x4 ra[IA];
+  int offa[IA], offb[IB];
+#pragma unroll
+  for (int i = 0; i < IA; ++i) {
+    const int r0 = (wave + 4 * i) * kBigRowsPerDma, row = r0 + lane / 4, slot = lane % 4;
+    int src;  // weight row of stage row `row`
+    if (MODE == kModeSwiglu) {
+      const int grp = r0 / 64;  // 0: gate, 1: up, 2: gate + 64, 3: up + 64 (uniform per instruction)
+      ra[i] = big_rsrc((grp & 1) ? a.a1 : a.a0, a_bytes);
+      src = f0 + 64 * (grp >> 1) + (row - 64 * grp);
+    } else {
+      ra[i] = big_rsrc(a.a0, a_bytes);
+      src = f0 + row;
+    }
+    offa[i] = (src * a.K + 8 * (slot ^ big_swz(row))) * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < IB; ++i) {
+    const int row = (wave + 4 * i) * kBigRowsPerDma + lane / 4, slot = lane % 4;
+    const int m = m0 + row;
+    const int src = m < a.k_tokens ? (MODE == kModeSwiglu ? a.idx[m] : m) : -1;
+    const bool ok = src >= 0 && (MODE != kModeSwiglu || src < a.n_rows);
+    offb[i] = ok ? (src * a.K + 8 * (slot ^ big_swz(row))) * 2 : (int)kBigOob;
+  }
+  auto dma = [&](uint32_t lds_byte, const u32x4& rs, int off) __attribute__((always_inline)) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_byte), "v"(off), "s"(rs)
+                 : "memory", "m0");
+  };
+  auto issue = [&](int sl) __attribute__((always_inline)) {  // slice sl into stage sl % kBigStages
+    const uint32_t st = lds_base + (uint32_t)((sl % kBigStages) * STAGE);
+    const int kb = sl * kBigRowBytes;
+#pragma unroll
+    for (int i = 0; i < IA; ++i) dma(st + (uint32_t)((wave + 4 * i) * 1024), ra[i], offa[i] + kb);
+#pragma unroll
+    for (int i = 0; i < IB; ++i) dma(st + (uint32_t)(TA * kBigRowBytes + (wave + 4 * i) * 1024), rx, offb[i] + kb);
+  };
+  f32x16 acc[WA][WB];
+#pragma unroll
+  for (int x = 0; x < WA; ++x)
+#pragma unroll
+    for (int y = 0; y < WB; ++y) acc[x][y] = f32x16{};
+  const int nsl = a.K / kBigBK;
+#pragma unroll
+  for (int sl = 0; sl < kBigStages - 1; ++sl)
+    if (sl < nsl) issue(sl);
+  auto rd = [&](const char* base, int row, int c) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(base + row * kBigRowBytes + 16 * (c ^ big_swz(row)));
+  };
+  constexpr int kVm = (kBigStages - 2) * (IA + IB);  // this wave's DMA of the slices after the next
+  static_assert(kVm < 64, "vmcnt immediate");
+  for (int sl = 0; sl < nsl; ++sl) {
+    // slice sl has landed for this wave (the kBigStages - 2 younger slices may
+    // still fly), then for every wave; the barrier also retires the reads of
+    // the stage the next issue overwrites
+    if (sl + kBigStages - 2 < nsl)
+      __builtin_amdgcn_s_waitcnt(big_wait_vm(kVm));
+    else
+      __builtin_amdgcn_s_waitcnt(big_wait_vm(0));
+    __syncthreads();
+    if (sl + kBigStages - 1 < nsl) issue(sl + kBigStages - 1);
+    const char* st = lds + (sl % kBigStages) * STAGE;
+    bf16x8 fa[KSTEPS][WA], fb[KSTEPS][WB];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+      for (int x = 0; x < WA; ++x) fa[ks][x] = rd(st, 32 * (WA * wa + x) + lrow, 2 * ks + lg);
+#pragma unroll
+      for (int y = 0; y < WB; ++y) fb[ks][y] = rd(st + TA * kBigRowBytes, 32 * (WB * wb + y) + lrow, 2 * ks + lg);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int x = 0; x < WA; ++x)
+#pragma unroll
+        for (int y = 0; y < WB; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][x], fb[ks][y], acc[x][y], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, KSTEPS * (WA + WB), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, KSTEPS * WA * WB, 0);
+  }
+
+  // lane holds token row m0 + 32 (WB wb + y) + lrow and features 8 (i/4) + 4 lg + i%4 of each block
+#pragma unroll
+  for (int y = 0; y < WB; ++y) {
+    const int m = m0 + 32 * (WB * wb + y) + lrow;
+    if (m >= a.k_tokens) continue;
+    if (MODE == kModeSwiglu) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        uint16_t* orow = a.out + (size_t)m * a.out_ld + f0 + 64 * wa + 32 * x;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          uint32_t w[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            uint32_t pk = 0;
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) {
+              const int i = 4 * g4 + 2 * e + hl;
+              const float g = acc[x][y][i], u = acc[x + 2][y][i];
+              const float act = g / (1.f + __expf(-g)) * u;
+              pk |= (uint32_t)float_to_bf16_bits(act) << (16 * hl);
+            }
+            w[e] = pk;
+          }
+          *reinterpret_cast<u32x2*>(orow + 8 * g4 + 4 * lg) = u32x2{w[0], w[1]};
+        }
+      }
+    } else {
+      const int dst = a.idx ? a.idx[m] : m;  // no index list: row m itself
+      if (dst < 0 || dst >= a.n_rows) continue;  // out-of-range index: row skipped
+#pragma unroll
+      for (int x = 0; x < WA; ++x) {
+        uint16_t* orow = a.out + (size_t)dst * a.out_ld + f0 + 32 * (WA * wa + x);
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          uint16_t* p = orow + 8 * g4 + 4 * lg;
+          const u32x2 old = *reinterpret_cast<const u32x2*>(p);
+          uint32_t w[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            uint32_t pk = 0;
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) {
+              const int i = 4 * g4 + 2 * e + hl;
+              const float h = bf16_bits_to_float((uint16_t)(old[e] >> (16 * hl)));
+              pk |= (uint32_t)float_to_bf16_bits(h + acc[x][y][i]) << (16 * hl);
+            }
+            w[e] = pk;
+          }
+          *reinterpret_cast<u32x2*>(p) = u32x2{w[0], w[1]};
+        }
+      }
+    }
+  }
+}
+
+// The large-tile path, when the launch has at least one work-group per CU and
+// every buffer fits the 32-bit offsets of a buffer load; returns false to let
+// the caller take the general kernel.
+template <int MODE>
+bool launch_ffn_big(const FfnArgs& g, int n_features, int rows, size_t a_bytes, size_t x_bytes, hipStream_t s) {
+  constexpr int WA = MODE == kModeSwiglu ? 4 : 2, WB = 4;
+  constexpr int TB = 64 * WB, FEAT = MODE == kModeSwiglu ? 128 : 64 * WA;
+  constexpr int LDS = kBigStages * (64 * WA + TB) * kBigRowBytes;
+  if (g.K % kBigBK != 0 || n_features % FEAT != 0) return false;
+  if (a_bytes >= (size_t)INT_MAX || x_bytes >= (size_t)INT_MAX) return false;
+  const dim3 grid(n_features / FEAT, cdiv(rows, TB));
+  if ((int64_t)grid.x * grid.y < 256) return false;
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute((const void*)ffn_big_kernel<MODE, WA, WB>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+  });
+  if (attr != hipSuccess) return false;
+  ffn_big_kernel<MODE, WA, WB><<<grid, kFfnThreads, LDS, s>>>(g, (uint32_t)a_bytes, (uint32_t)x_bytes);
+  return true;
+}
+
 // ---- layer glue: fused QKV projection + RoPE + append of the query rows' K/V ----
 //
 // paooo.com "如何使用RedKnot" (EXECUTE recomputes the query segment) and RedKnot
@@ -366,17 +575,20 @@ extern "C" int32_t sparse_ffn_swiglu(void* hidden, int32_t n_rows, int32_t hidde
   if (!aligned16(hidden) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(workspace))
     return fail(SEGKV_ERR_ALIGNMENT, "tensors must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* act = static_cast<uint16_t*>(workspace);  // the activation [k][inter]
   FfnArgs g1;
   g1.a0 = static_cast<const uint16_t*>(w_gate);
   g1.a1 = static_cast<const uint16_t*>(w_up);
   g1.x = static_cast<const uint16_t*>(hidden);
-  g1.out = static_cast<uint16_t*>(workspace);
+  g1.out = act;
   g1.idx = idx_dev;
   g1.k_tokens = k;
   g1.K = hidden_size;
   g1.out_ld = inter;
   g1.n_rows = n_rows;
-  if (small_grid(inter / 64, k))
+  if (launch_ffn_big<kModeSwiglu>(g1, inter, k, (size_t)inter * hidden_size * 2, (size_t)n_rows * hidden_size * 2, s))
+    ;
+  else if (small_grid(inter / 64, k))
     ffn_gemm_kernel<kModeSwiglu, 1><<<dim3(inter / 64, cdiv(k, 64)), kFfnThreads, 0, s>>>(g1);
   else
     ffn_gemm_kernel<kModeSwiglu, 2><<<dim3(inter / 64, cdiv(k, kRowsB)), kFfnThreads, 0, s>>>(g1);
@@ -384,14 +596,16 @@ extern "C" int32_t sparse_ffn_swiglu(void* hidden, int32_t n_rows, int32_t hidde
   FfnArgs g2;
   g2.a0 = static_cast<const uint16_t*>(w_down);
   g2.a1 = nullptr;
-  g2.x = static_cast<const uint16_t*>(workspace);
+  g2.x = act;
   g2.out = static_cast<uint16_t*>(hidden);
   g2.idx = idx_dev;
   g2.k_tokens = k;
   g2.K = inter;
   g2.out_ld = hidden_size;
   g2.n_rows = n_rows;
-  if (small_grid(hidden_size / kRowsA, k))
+  if (launch_ffn_big<kModeResidual>(g2, hidden_size, k, (size_t)hidden_size * inter * 2, (size_t)k * inter * 2, s))
+    ;
+  else if (small_grid(hidden_size / kRowsA, k))
     ffn_gemm_kernel<kModeResidual, 1><<<dim3(hidden_size / kRowsA, cdiv(k, 64)), kFfnThreads, 0, s>>>(g2);
   else
     ffn_gemm_kernel<kModeResidual, 2><<<dim3(hidden_size / kRowsA, cdiv(k, kRowsB)), kFfnThreads, 0, s>>>(g2);
