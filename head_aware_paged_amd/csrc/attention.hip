@@ -160,14 +160,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
   __shared__ int s_simd[kAttnWaves];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(a.plan);
-  const MTile* mts = reinterpret_cast<const MTile*>(a.plan + a.L.mtiles_off);
   const Item* items = reinterpret_cast<const Item*>(a.plan + a.L.items_off);
-  if ((int)blockIdx.x >= hdr->n_items) return;
+  // The item record holds everything the work-group needs from the plan; it
+  // is read together with the header's item count (the grid never exceeds
+  // the items region the host sized for this layout), one round trip.
   const Item it = items[blockIdx.x];
-  if (it.mtile < 0) return;  // empty slot of the XCD-aware order
-  const MTile mt = mts[it.mtile];
-  const int t_lo = chunk_tile_lo(mt.n_tiles, mt.n_chunks, it.chunk);
-  const int T = chunk_tile_lo(mt.n_tiles, mt.n_chunks, it.chunk + 1) - t_lo;
+  const int n_items = hdr->n_items;
+  if ((int)blockIdx.x >= n_items || it.mtile < 0) return;  // empty slot of the XCD-aware order
+  const int T = it.T;
   if (T <= 0) return;  // every m-tile chunk holds a tile (each row sees its own key)
 
   const int tid = threadIdx.x;
@@ -176,24 +176,24 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
   const int MP = kMRows / a.G;
   const int rm = wave * 32 + lrow;               // row within the m-tile
   const int hg = rm / MP, p = rm % MP;
-  const bool row_valid = p < mt.n_pos;
-  const int pc = row_valid ? p : mt.n_pos - 1;    // padding rows mirror the last valid row
-  const int qhead = mt.h * a.G + hg;
-  const int qrow = mt.q_row0 + pc;
-  const int pos = mt.pos0 + pc;
-  const bool is_local = mt.cls == kClassLocal;
-  const int lo_row = is_local ? local_lo(pos, mt.bq, mt.W) : 0;
-  const int pos_min = mt.pos0, pos_max = mt.pos0 + mt.n_pos - 1;
-  const int lo_max = is_local ? local_lo(pos_max, mt.bq, mt.W) : 0;
+  const bool row_valid = p < it.n_pos;
+  const int pc = row_valid ? p : it.n_pos - 1;    // padding rows mirror the last valid row
+  const int qhead = it.h * a.G + hg;
+  const int qrow = it.q_row0 + pc;
+  const int pos = it.pos0 + pc;
+  const bool is_local = it.cls == kClassLocal;
+  const int lo_row = is_local ? local_lo(pos, it.bq, it.W) : 0;
+  const int pos_min = it.pos0, pos_max = it.pos0 + it.n_pos - 1;
+  const int lo_max = is_local ? local_lo(pos_max, it.bq, it.W) : 0;
 
   // the item's page table -> LDS ring (entries past the m-tile's end, or with
   // an invalid page id, become pid -1 / pos INT_MAX); the first kRingTiles
   // tiles now, later ones by stage_table
-  const int e_lo = mt.e_begin + kTilePages * t_lo;
+  const int e_lo = it.e_lo;
   auto stage_entry = [&](int x) __attribute__((always_inline)) {  // entry x of the item
     const int e = e_lo + x;
     int pid = -1, ps = INT_MAX;
-    if (e < mt.e_end) {
+    if (e < it.e_end) {
       pid = a.page_ids[e];
       ps = a.page_pos[e];
       SEGKV_DCHECK(g_attn_check, pid >= 0 && pid < a.pool_pages, 1);
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
     if (kMask || !full) {
       if (kMask) {
         // bytes of keys ps + 8 lg .. + 7 of each page, this row
-        const uint8_t* mrow = a.mask + ((size_t)mt.h * a.mask_rows + qrow) * a.mask_L + 8 * lg;
+        const uint8_t* mrow = a.mask + ((size_t)it.h * a.mask_rows + qrow) * a.mask_L + 8 * lg;
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
           const uint64_t mb = ps4[pp] != INT_MAX ? *reinterpret_cast<const uint64_t*>(mrow + ps4[pp]) : 0;
@@ -411,6 +411,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
   // the integer above, so a rescale factor is an exact power of two), P(i) in
   // bf16, row sums of the unrounded probabilities in fp32
   auto softmax_step = [&](int i) __attribute__((always_inline)) {
+    // The other wave of this SIMD is in its matrix step meanwhile; its MFMAs
+    // and LDS reads cost this wave issue slots, and this (vector-ALU bound)
+    // step is the longer of the two, so it takes the higher issue priority
+    // while it runs. (The reverse, priority for the matrix step, is slower.)
+    __builtin_amdgcn_s_setprio(2);
     mask_if_needed(i);
     float mx[4];
 #pragma unroll
@@ -446,6 +451,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
     m_run = m_new;
     o_scale = alpha;
     o_scale_due = __builtin_amdgcn_ballot_w64(grow) != 0;
+    __builtin_amdgcn_s_setprio(0);
   };
   auto last_pv = [&](const char* vbuf) __attribute__((always_inline)) {
     rescale_o();
@@ -547,7 +553,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
   // goes to a per-wave [32 rows][D] block, 16-byte chunks XOR-swizzled by
   // row, and comes back whole rows per instruction, so every store writes
   // full rows (writing the fragments directly puts 32 rows in every store)
-  const bool split = mt.partial_base >= 0;
+  const bool split = it.partial_slot >= 0;
   const float inv = l_row > 0.f ? 1.f / l_row : 0.f;  // a chunk may hold no key of a row: O_c = 0, l_c = 0
   __syncthreads();  // every wave's last PV product has read its V stage
   constexpr int OCH = D / 8;  // 16-byte chunks per row
@@ -561,7 +567,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
           bf16x4{(__bf16)(o_acc[b][4 * g4 + 0] * inv), (__bf16)(o_acc[b][4 * g4 + 1] * inv),
                  (__bf16)(o_acc[b][4 * g4 + 2] * inv), (__bf16)(o_acc[b][4 * g4 + 3] * inv)};
     }
-  char* slot = split ? a.partials + (size_t)(mt.partial_base + it.chunk) * partial_slot_bytes(D) : nullptr;
+  char* slot = split ? a.partials + (size_t)it.partial_slot * partial_slot_bytes(D) : nullptr;
   constexpr int RPI = 64 / OCH;  // rows per read-back instruction
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
@@ -570,8 +576,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_main_kernel(AttnArgs a) 
     const int rmr = wave * 32 + r, hgr = rmr / MP, pr = rmr % MP;
     if (split) {
       *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(slot) + (size_t)rmr * D + 8 * c) = v;
-    } else if (pr < mt.n_pos) {
-      *reinterpret_cast<u32x4*>(a.out + ((size_t)(mt.q_row0 + pr) * a.Hq + mt.h * a.G + hgr) * D + 8 * c) = v;
+    } else if (pr < it.n_pos) {
+      *reinterpret_cast<u32x4*>(a.out + ((size_t)(it.q_row0 + pr) * a.Hq + it.h * a.G + hgr) * D + 8 * c) = v;
     }
   }
   if (lg == 0) {
@@ -593,10 +599,11 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
   constexpr int DG = D / 4;                       // 4-element groups per row
   constexpr int kRowsPerBlock = kCombineThreads / DG;
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(a.plan);
-  if ((int)blockIdx.x >= hdr->n_split) return;
-  const MTile* mts = reinterpret_cast<const MTile*>(a.plan + a.L.mtiles_off);
-  const int32_t* split = reinterpret_cast<const int32_t*>(a.plan + a.L.split_off);
-  const MTile mt = mts[split[blockIdx.x]];
+  // the split record and the header's count in one round trip (the grid
+  // never exceeds the split region the host sized for this layout)
+  const SplitTile mt = reinterpret_cast<const SplitTile*>(a.plan + a.L.split_off)[blockIdx.x];
+  const int n_split = hdr->n_split;
+  if ((int)blockIdx.x >= n_split) return;
   const int MP = kMRows / a.G;
   const int rm = blockIdx.y * kRowsPerBlock + threadIdx.x / DG, dg = threadIdx.x % DG;
   const int hg = rm / MP, p = rm % MP;

@@ -295,7 +295,7 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
   int32_t* req_off_g = reinterpret_cast<int32_t*>(a.plan + a.L.req_mt_off);
   MTile* mt = reinterpret_cast<MTile*>(a.plan + a.L.mtiles_off);
   Item* items = reinterpret_cast<Item*>(a.plan + a.L.items_off);
-  int32_t* split = reinterpret_cast<int32_t*>(a.plan + a.L.split_off);
+  SplitTile* split = reinterpret_cast<SplitTile*>(a.plan + a.L.split_off);
   const int MP = mtile_positions(a.G);
   const int S = a.chunk_tiles;
 
@@ -387,7 +387,10 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
       [&](int i, const int (&p)[2]) {
         if (mt_chunks[i] > 1) {
           mt[i].partial_base = p[0];
-          if (p[1] < a.n_split) split[p[1]] = i;
+          if (p[1] < a.n_split) {
+            const MTile& d = mt[i];  // written by this work-group before the scan's barriers
+            split[p[1]] = SplitTile{p[0], mt_chunks[i], d.q_row0, d.h, d.n_pos, {0, 0, 0}};
+          }
         }
       },
       mt_tot, s);
@@ -417,7 +420,8 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
   const int q8 = a.n_items / kXcds;
   for (int b = tid; b < a.n_items; b += kScanThreads) {
     const int p = (b & (kXcds - 1)) * q8 + (b >> 3);
-    Item it{-1, 0};
+    Item it{};
+    it.mtile = -1;
     if (p < n_pos) {
       int lo = 0, hi = n_pairs - 1;  // pair: last k with pair_ib[k] <= p
       while (lo < hi) {
@@ -427,7 +431,23 @@ __global__ __launch_bounds__(kScanThreads) void build_kernel(PagesArgs a, int fi
       const int k = lo, r = k / a.Hkv, h = k % a.Hkv;
       const int nj = (req_off[r + 1] - req_off[r]) / a.Hkv;
       const int rel = p - pair_ib[k], c = rel / nj, i = req_off[r] + h * nj + rel % nj;
-      if (c < mt_chunks[i]) it = Item{i, c};
+      if (c < mt_chunks[i]) {
+        const MTile d = mt[i];  // complete since the scans' barriers
+        it.mtile = i;
+        it.chunk = c;
+        it.t_lo = chunk_tile_lo(d.n_tiles, d.n_chunks, c);
+        it.T = chunk_tile_lo(d.n_tiles, d.n_chunks, c + 1) - it.t_lo;
+        it.h = d.h;
+        it.q_row0 = d.q_row0;
+        it.n_pos = d.n_pos;
+        it.pos0 = d.pos0;
+        it.cls = d.cls;
+        it.W = d.W;
+        it.bq = d.bq;
+        it.e_lo = d.e_begin + kTilePages * it.t_lo;
+        it.e_end = d.e_end;
+        it.partial_slot = d.partial_base >= 0 ? d.partial_base + c : -1;
+      }
     }
     items[b] = it;
   }

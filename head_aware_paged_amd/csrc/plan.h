@@ -206,8 +206,23 @@ struct MTile {
   int32_t pad[3];
 };
 
+// An attention work item: one chunk of one m-tile, with the m-tile facts its
+// work-group needs, so that the item is the only plan record it reads.
 struct Item {
-  int32_t mtile, chunk;  // mtile < 0: empty slot, the work-group exits
+  int32_t mtile, chunk;    // mtile < 0: empty slot, the work-group exits
+  int32_t t_lo, T;         // the chunk's key tiles [t_lo, t_lo + T) of the m-tile
+  int32_t h, q_row0, n_pos, pos0;
+  int32_t cls, W, bq;
+  int32_t e_lo;            // absolute table entry of the chunk's first tile
+  int32_t e_end;           // absolute table entry past the m-tile's last one
+  int32_t partial_slot;    // the chunk's split-KV partial slot, -1 when the m-tile is not split
+  int32_t pad[2];
+};
+
+// A split m-tile as its combine work-group reads it.
+struct SplitTile {
+  int32_t partial_base, n_chunks, q_row0, h, n_pos;
+  int32_t pad[3];
 };
 
 // XCD-aware item order. Work-groups are dispatched round-robin over the 8 XCDs
@@ -250,7 +265,7 @@ SEGKV_HD PlanLayout plan_layout(int n_pairs, int n_requests, int n_mtiles, int n
   L.mtiles_off = L.req_mt_off + align256(sizeof(int32_t) * (size_t)(n_requests + 1));
   L.items_off = L.mtiles_off + align256(sizeof(MTile) * (size_t)imax(n_mtiles, 1));
   L.split_off = L.items_off + align256(sizeof(Item) * (size_t)imax(n_items, 1));
-  L.imp_items_off = L.split_off + align256(sizeof(int32_t) * (size_t)imax(n_split, 1));
+  L.imp_items_off = L.split_off + align256(sizeof(SplitTile) * (size_t)imax(n_split, 1));
   L.req_key_off = L.imp_items_off + align256(sizeof(ImpItem) * (size_t)imax(n_imp_items, 1));
   L.imp_mask_off = L.req_key_off + align256(sizeof(int32_t) * (size_t)(n_requests + 1));
   L.total = L.imp_mask_off + align256(sizeof(uint64_t) * (size_t)n_requests * (size_t)imax(key_blocks, 1));
