@@ -136,3 +136,19 @@ def test_topk_select_signed_scores():
     segkv_topk_select(torch.from_numpy(x).cuda(), n, k, idx)
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy(), oracle.topk_select(x, k))
+
+
+@pytest.mark.parametrize("n,k", [(33280, 8320), (1000, 999), (70000, 17)])
+def test_topk_select_narrow_range(n, k):
+    """Keys that share their leading 19 bits (1 + [0, 2^-12) in fp32: about
+    2,048 distinct values, so many ties): the first radix passes see a single
+    bin, the k-th key is resolved by the low bits, and ties go to the lower
+    index."""
+    print(f"case topk narrow range n={n} k={k}", flush=True)
+    x = (np.float32(1.0) + workloads.uniform_f32(seed=n + 3 * k, n=n, lo=0.0, hi=2.0 ** -12)).astype(np.float32)
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    from head_aware_paged_amd import segkv_topk_select
+    segkv_topk_select(torch.from_numpy(x).cuda(), n, k, idx)
+    torch.cuda.synchronize()
+    ref = sorted(sorted(range(n), key=lambda j: (-float(x[j]), j))[:k])
+    assert idx.cpu().numpy().tolist() == ref
