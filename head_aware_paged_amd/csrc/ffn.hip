@@ -229,50 +229,22 @@ __device__ __forceinline__ u32x4 big_rsrc(const void* base, uint32_t bytes) {
 }
 __device__ __forceinline__ int big_swz(int row) { return (row >> 2) & 3; }
 
-// MODE kModeSwiglu: WA = 4; the A tile's 256 rows are gate rows f0 .. f0+63,
-// up rows f0 .. f0+63, gate rows f0+64 .., up rows f0+64 .. (64-row groups),
-// so wave wa holds gate blocks 0, 1 and the matching up blocks 2, 3 of
-// features f0 + 64 wa ... The work-group covers 128 features.
-template <int MODE, int WA, int WB>
-__global__ __launch_bounds__(kFfnThreads, 1) void ffn_big_kernel(FfnArgs a, uint32_t a_bytes, uint32_t x_bytes) {
+// Main loop of the large-tile path: acc[x][y] (wave block x of the A tile,
+// block y of the token tile) over K. For each of its DMA instructions (one
+// per 16-row group: A groups wave, wave + 4, ..., then the token groups alike)
+// the wave passes the source buffer and the byte offset at k = 0 of the
+// lane's 16-byte chunk (row (wave + 4 i) * 16 + lane / 4, chunk lane % 4 at
+// slot chunk ^ big_swz(row)); kBigOob reads a zero row.
+template <int WA, int WB>
+__device__ __forceinline__ void big_mainloop(const u32x4 (&ra)[WA], const int (&offa)[WA], const u32x4& rx,
+                                             const int (&offb)[WB], int K, char* lds, f32x16 (&acc)[WA][WB]) {
   constexpr int TA = 64 * WA, TB = 64 * WB;
-  constexpr int IA = TA / kBigRowsPerDma / 4, IB = TB / kBigRowsPerDma / 4;  // DMA instructions per wave and slice
   constexpr int STAGE = (TA + TB) * kBigRowBytes;
   constexpr int KSTEPS = kBigBK / 16;
-  static_assert(MODE != kModeSwiglu || WA == 4, "SwiGLU tile pairs gate and up blocks");
-  extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lrow = lane & 31, lg = lane >> 5;
   const int wa = wave & 1, wb = wave >> 1;
-  const int f0 = blockIdx.x * (MODE == kModeSwiglu ? 128 : TA);  // first output feature
-  const int m0 = blockIdx.y * TB;                                 // first token row
   const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
-  const u32x4 rx = big_rsrc(a.x, x_bytes);
-  // this wave's DMA rows: instruction i covers stage rows (wave + 4 i) * 16 ..
-  u32x4 ra[IA];
-  int offa[IA], offb[IB];
-#pragma unroll
-  for (int i = 0; i < IA; ++i) {
-    const int r0 = (wave + 4 * i) * kBigRowsPerDma, row = r0 + lane / 4, slot = lane % 4;
-    int src;  // weight row of stage row `row`
-    if (MODE == kModeSwiglu) {
-      const int grp = r0 / 64;  // 0: gate, 1: up, 2: gate + 64, 3: up + 64 (uniform per instruction)
-      ra[i] = big_rsrc((grp & 1) ? a.a1 : a.a0, a_bytes);
-      src = f0 + 64 * (grp >> 1) + (row - 64 * grp);
-    } else {
-      ra[i] = big_rsrc(a.a0, a_bytes);
-      src = f0 + row;
-    }
-    offa[i] = (src * a.K + 8 * (slot ^ big_swz(row))) * 2;
-  }
-#pragma unroll
-  for (int i = 0; i < IB; ++i) {
-    const int row = (wave + 4 * i) * kBigRowsPerDma + lane / 4, slot = lane % 4;
-    const int m = m0 + row;
-    const int src = m < a.k_tokens ? (MODE == kModeSwiglu ? a.idx[m] : m) : -1;
-    const bool ok = src >= 0 && (MODE != kModeSwiglu || src < a.n_rows);
-    offb[i] = ok ? (src * a.K + 8 * (slot ^ big_swz(row))) * 2 : (int)kBigOob;
-  }
   auto dma = [&](uint32_t lds_byte, const u32x4& rs, int off) __attribute__((always_inline)) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_byte), "v"(off), "s"(rs)
                  : "memory", "m0");
@@ -281,23 +253,22 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_big_kernel(FfnArgs a, uint
     const uint32_t st = lds_base + (uint32_t)((sl % kBigStages) * STAGE);
     const int kb = sl * kBigRowBytes;
 #pragma unroll
-    for (int i = 0; i < IA; ++i) dma(st + (uint32_t)((wave + 4 * i) * 1024), ra[i], offa[i] + kb);
+    for (int i = 0; i < WA; ++i) dma(st + (uint32_t)((wave + 4 * i) * 1024), ra[i], offa[i] + kb);
 #pragma unroll
-    for (int i = 0; i < IB; ++i) dma(st + (uint32_t)(TA * kBigRowBytes + (wave + 4 * i) * 1024), rx, offb[i] + kb);
+    for (int i = 0; i < WB; ++i) dma(st + (uint32_t)(TA * kBigRowBytes + (wave + 4 * i) * 1024), rx, offb[i] + kb);
   };
-  f32x16 acc[WA][WB];
 #pragma unroll
   for (int x = 0; x < WA; ++x)
 #pragma unroll
     for (int y = 0; y < WB; ++y) acc[x][y] = f32x16{};
-  const int nsl = a.K / kBigBK;
+  const int nsl = K / kBigBK;
 #pragma unroll
   for (int sl = 0; sl < kBigStages - 1; ++sl)
     if (sl < nsl) issue(sl);
   auto rd = [&](const char* base, int row, int c) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x8*>(base + row * kBigRowBytes + 16 * (c ^ big_swz(row)));
   };
-  constexpr int kVm = (kBigStages - 2) * (IA + IB);  // this wave's DMA of the slices after the next
+  constexpr int kVm = (kBigStages - 2) * (WA + WB);  // this wave's DMA of the slices after the next
   static_assert(kVm < 64, "vmcnt immediate");
   for (int sl = 0; sl < nsl; ++sl) {
     // slice sl has landed for this wave (the kBigStages - 2 younger slices may
@@ -328,6 +299,60 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_big_kernel(FfnArgs a, uint
     __builtin_amdgcn_sched_group_barrier(0x100, KSTEPS * (WA + WB), 0);
     __builtin_amdgcn_sched_group_barrier(0x008, KSTEPS * WA * WB, 0);
   }
+}
+
+// Byte offset at k = 0 of this lane's chunk of token-tile DMA group i: token
+// row `row` of x (kBigOob when row < 0).
+template <int WB>
+__device__ __forceinline__ void big_token_offsets(int (&offb)[WB], int wave, int lane, int K,
+                                                  const int (&src)[WB]) {
+#pragma unroll
+  for (int i = 0; i < WB; ++i) {
+    const int row = (wave + 4 * i) * kBigRowsPerDma + lane / 4, slot = lane % 4;
+    offb[i] = src[i] >= 0 ? (src[i] * K + 8 * (slot ^ big_swz(row))) * 2 : (int)kBigOob;
+  }
+}
+
+// MODE kModeSwiglu: WA = 4; the A tile's 256 rows are gate rows f0 .. f0+63,
+// up rows f0 .. f0+63, gate rows f0+64 .., up rows f0+64 .. (64-row groups),
+// so wave wa holds gate blocks 0, 1 and the matching up blocks 2, 3 of
+// features f0 + 64 wa ... The work-group covers 128 features.
+// OCC: work-groups per CU the launch bounds allow (1 for the 256x256 tiles).
+template <int MODE, int WA, int WB, int OCC>
+__global__ __launch_bounds__(kFfnThreads, OCC) void ffn_big_kernel(FfnArgs a, uint32_t a_bytes, uint32_t x_bytes) {
+  constexpr int TA = 64 * WA, TB = 64 * WB;
+  static_assert(MODE != kModeSwiglu || WA == 4, "SwiGLU tile pairs gate and up blocks");
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int lrow = lane & 31, lg = lane >> 5;
+  const int wa = wave & 1, wb = wave >> 1;
+  const int f0 = blockIdx.x * (MODE == kModeSwiglu ? 128 : TA);  // first output feature
+  const int m0 = blockIdx.y * TB;                                 // first token row
+  u32x4 ra[WA];
+  int offa[WA], offb[WB], srcb[WB];
+#pragma unroll
+  for (int i = 0; i < WA; ++i) {
+    const int r0 = (wave + 4 * i) * kBigRowsPerDma, row = r0 + lane / 4, slot = lane % 4;
+    int src;  // weight row of stage row `row`
+    if (MODE == kModeSwiglu) {
+      const int grp = r0 / 64;  // 0: gate, 1: up, 2: gate + 64, 3: up + 64 (uniform per instruction)
+      ra[i] = big_rsrc((grp & 1) ? a.a1 : a.a0, a_bytes);
+      src = f0 + 64 * (grp >> 1) + (row - 64 * grp);
+    } else {
+      ra[i] = big_rsrc(a.a0, a_bytes);
+      src = f0 + row;
+    }
+    offa[i] = (src * a.K + 8 * (slot ^ big_swz(row))) * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < WB; ++i) {
+    const int m = m0 + (wave + 4 * i) * kBigRowsPerDma + lane / 4;
+    const int src = m < a.k_tokens ? (MODE == kModeSwiglu ? a.idx[m] : m) : -1;
+    srcb[i] = src >= 0 && (MODE != kModeSwiglu || src < a.n_rows) ? src : -1;
+  }
+  big_token_offsets<WB>(offb, wave, lane, a.K, srcb);
+  f32x16 acc[WA][WB];
+  big_mainloop<WA, WB>(ra, offa, big_rsrc(a.x, x_bytes), offb, a.K, lds, acc);
 
   // lane holds token row m0 + 32 (WB wb + y) + lrow and features 8 (i/4) + 4 lg + i%4 of each block
 #pragma unroll
@@ -385,9 +410,18 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_big_kernel(FfnArgs a, uint
   }
 }
 
-// The large-tile path, when the launch has at least one work-group per CU and
-// every buffer fits the 32-bit offsets of a buffer load; returns false to let
-// the caller take the general kernel.
+// Dynamic LDS above the default limit is allowed once per kernel.
+template <auto* KERNEL>
+bool big_lds_attr(int bytes) {
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [bytes] { attr = hipFuncSetAttribute((const void*)KERNEL, hipFuncAttributeMaxDynamicSharedMemorySize, bytes); });
+  return attr == hipSuccess;
+}
+
+// The 256x256 large-tile path of the sparse FFN, when the launch has at least
+// one work-group per CU and every buffer fits the 32-bit offsets of a buffer
+// load; returns false to let the caller take the general kernel.
 template <int MODE>
 bool launch_ffn_big(const FfnArgs& g, int n_features, int rows, size_t a_bytes, size_t x_bytes, hipStream_t s) {
   constexpr int WA = MODE == kModeSwiglu ? 4 : 2, WB = 4;
@@ -397,14 +431,8 @@ bool launch_ffn_big(const FfnArgs& g, int n_features, int rows, size_t a_bytes, 
   if (a_bytes >= (size_t)INT_MAX || x_bytes >= (size_t)INT_MAX) return false;
   const dim3 grid(n_features / FEAT, cdiv(rows, TB));
   if ((int64_t)grid.x * grid.y < 256) return false;
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [] {
-    attr = hipFuncSetAttribute((const void*)ffn_big_kernel<MODE, WA, WB>,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-  });
-  if (attr != hipSuccess) return false;
-  ffn_big_kernel<MODE, WA, WB><<<grid, kFfnThreads, LDS, s>>>(g, (uint32_t)a_bytes, (uint32_t)x_bytes);
+  if (!big_lds_attr<ffn_big_kernel<MODE, WA, WB, 1>>(LDS)) return false;
+  ffn_big_kernel<MODE, WA, WB, 1><<<grid, kFfnThreads, LDS, s>>>(g, (uint32_t)a_bytes, (uint32_t)x_bytes);
   return true;
 }
 
@@ -527,6 +555,88 @@ __global__ __launch_bounds__(kFfnThreads, 2) void qkv_rope_append_kernel(QkvArgs
           const float2 cs = a.rope_cs[(size_t)m * half + j + e];
           lo4[e] = x * cs.x - y * cs.y;
           hi4[e] = x * cs.y + y * cs.x;
+        }
+      }
+      if (kind == 2) {  // d-major page: element (d, slot) at d * P + slot
+        uint16_t* vp = a.v_pool + (size_t)(slot / kPage) * a.D * kPage + slot % kPage;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vp[(size_t)(j + e) * kPage] = float_to_bf16_bits(lo4[e]);
+          vp[(size_t)(j + e + half) * kPage] = float_to_bf16_bits(hi4[e]);
+        }
+      } else {
+        uint16_t* dst = kind == 0 ? a.q_out + ((size_t)m * a.Hq + head) * a.D : a.k_pool + (size_t)slot * a.D;
+        const u32x2 wl = {(uint32_t)float_to_bf16_bits(lo4[0]) | (uint32_t)float_to_bf16_bits(lo4[1]) << 16,
+                          (uint32_t)float_to_bf16_bits(lo4[2]) | (uint32_t)float_to_bf16_bits(lo4[3]) << 16};
+        const u32x2 wh = {(uint32_t)float_to_bf16_bits(hi4[0]) | (uint32_t)float_to_bf16_bits(hi4[1]) << 16,
+                          (uint32_t)float_to_bf16_bits(hi4[2]) | (uint32_t)float_to_bf16_bits(hi4[3]) << 16};
+        *reinterpret_cast<u32x2*>(dst + j) = wl;
+        *reinterpret_cast<u32x2*>(dst + j + half) = wh;
+      }
+    }
+  }
+}
+
+// The QKV projection on the large-tile main loop: 128 weight rows x 64 WB
+// token rows per work-group (OCC per CU). The A tile is one head (D = 128)
+// or two (D = 64). For D = 128 its middle two 32-row blocks are swapped in
+// LDS (stage blocks 0..3 = dims 0-31, 64-95, 32-63, 96-127), so that each
+// wave's two blocks are dims j0 .. j0 + 31 and j0 + 64 ..: the rotate-half
+// pairs, as in qkv_rope_append_kernel, whose epilogue this one repeats.
+template <int WB, int OCC>
+__global__ __launch_bounds__(kFfnThreads, OCC) void qkv_big_kernel(QkvArgs a, uint32_t w_bytes, uint32_t x_bytes) {
+  constexpr int WA = 2, TB = 64 * WB;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int lrow = lane & 31, lg = lane >> 5;
+  const int wa = wave & 1, wb = wave >> 1;
+  const int n0 = blockIdx.x * 128, m0 = blockIdx.y * TB;
+  const int nfeat = (a.Hq + 2 * a.Hkv) * a.D;
+  u32x4 ra[WA];
+  int offa[WA], offb[WB], srcb[WB];
+#pragma unroll
+  for (int i = 0; i < WA; ++i) {
+    const int row = (wave + 4 * i) * kBigRowsPerDma + lane / 4, slot = lane % 4;
+    const int blk = row / 32, sb = a.D == 128 && (blk == 1 || blk == 2) ? 3 - blk : blk;
+    const int f = n0 + 32 * sb + row % 32;  // weight row (feature) of stage row `row`
+    ra[i] = big_rsrc(a.w, w_bytes);
+    offa[i] = f < nfeat ? (f * a.K + 8 * (slot ^ big_swz(row))) * 2 : (int)kBigOob;
+  }
+#pragma unroll
+  for (int i = 0; i < WB; ++i) {
+    const int m = m0 + (wave + 4 * i) * kBigRowsPerDma + lane / 4;
+    srcb[i] = m < a.T ? m : -1;
+  }
+  big_token_offsets<WB>(offb, wave, lane, a.K, srcb);
+  f32x16 acc[WA][WB];
+  big_mainloop<WA, WB>(ra, offa, big_rsrc(a.x, x_bytes), offb, a.K, lds, acc);
+
+  // acc[0][y][i] and acc[1][y][i]: dims j and j + D/2 of head `head`, token
+  // row m = m0 + 32 (WB wb + y) + lrow, with j = j0 + 8 (i/4) + 4 lg + i%4
+  const int head = (n0 + 64 * wa) / a.D, j0 = a.D == 128 ? 32 * wa : 0, half = a.D / 2;
+  if (head >= a.Hq + 2 * a.Hkv) return;  // the unused half of the last tile
+  const int kind = head < a.Hq ? 0 : head < a.Hq + a.Hkv ? 1 : 2;  // Q, K, V
+  const int hk = kind == 1 ? head - a.Hq : head - a.Hq - a.Hkv;
+#pragma unroll
+  for (int y = 0; y < WB; ++y) {
+    const int m = m0 + 32 * (WB * wb + y) + lrow;
+    if (m >= a.T) continue;
+    const int slot = kind == 0 ? 0 : a.row_slot[(size_t)m * a.Hkv + hk];
+    if (slot < 0) continue;  // no page for this row: nothing written
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int j = j0 + 8 * g4 + 4 * lg;
+      float lo4[4], hi4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = acc[0][y][4 * g4 + e], yv = acc[1][y][4 * g4 + e];
+        if (kind == 2) {
+          lo4[e] = x;
+          hi4[e] = yv;
+        } else {
+          const float2 cs = a.rope_cs[(size_t)m * half + j + e];
+          lo4[e] = x * cs.x - yv * cs.y;
+          hi4[e] = x * cs.y + yv * cs.x;
         }
       }
       if (kind == 2) {  // d-major page: element (d, slot) at d * P + slot
@@ -689,7 +799,13 @@ extern "C" int32_t segkv_qkv_rope_append(const segkv_dims* dims, const segkv_met
   a.Hkv = Hkv;
   a.D = D;
   const int nx = cdiv((Hq + 2 * Hkv) * D, kRowsA);
-  if (small_grid(nx, (int)T))
+  const size_t w_bytes = (size_t)(Hq + 2 * Hkv) * D * hidden_size * 2, x_bytes = (size_t)T * hidden_size * 2;
+  constexpr int kQkvWB = 2, kQkvLds = kBigStages * (128 + 64 * kQkvWB) * kBigRowBytes;
+  if (hidden_size % kBigBK == 0 && w_bytes < (size_t)INT_MAX && x_bytes < (size_t)INT_MAX &&
+      big_lds_attr<qkv_big_kernel<kQkvWB, 2>>(kQkvLds))
+    qkv_big_kernel<kQkvWB, 2><<<dim3(nx, cdiv((int)T, 64 * kQkvWB)), kFfnThreads, kQkvLds, s>>>(
+        a, (uint32_t)w_bytes, (uint32_t)x_bytes);
+  else if (small_grid(nx, (int)T))
     qkv_rope_append_kernel<1><<<dim3(nx, cdiv((int)T, 64)), kFfnThreads, 0, s>>>(a);
   else
     qkv_rope_append_kernel<2><<<dim3(nx, cdiv((int)T, kRowsB)), kFfnThreads, 0, s>>>(a);
@@ -719,7 +835,15 @@ extern "C" int32_t segkv_out_proj_residual(const void* attn, int32_t n_rows, int
   g.out_ld = hidden_size;
   g.n_rows = n_rows;
   const int nx = hidden_size / kRowsA;
-  if (small_grid(nx, n_rows))
+  // large-tile main loop, 128 x 64 tiles, two work-groups per CU (the same
+  // tile as the 64-row-token form of ffn_gemm_kernel, which stays for
+  // operands beyond 32-bit buffer offsets)
+  const size_t w_bytes = (size_t)hidden_size * in_features * 2, x_bytes = (size_t)n_rows * in_features * 2;
+  constexpr int kOpLds = kBigStages * (128 + 64) * kBigRowBytes;
+  if (w_bytes < (size_t)INT_MAX && x_bytes < (size_t)INT_MAX && big_lds_attr<ffn_big_kernel<kModeResidual, 2, 1, 2>>(kOpLds))
+    ffn_big_kernel<kModeResidual, 2, 1, 2><<<dim3(nx, cdiv(n_rows, 64)), kFfnThreads, kOpLds, hipStream_t(stream)>>>(
+        g, (uint32_t)w_bytes, (uint32_t)x_bytes);
+  else if (small_grid(nx, n_rows))
     ffn_gemm_kernel<kModeResidual, 1><<<dim3(nx, cdiv(n_rows, 64)), kFfnThreads, 0, hipStream_t(stream)>>>(g);
   else
     ffn_gemm_kernel<kModeResidual, 2><<<dim3(nx, cdiv(n_rows, kRowsB)), kFfnThreads, 0, hipStream_t(stream)>>>(g);
