@@ -713,8 +713,14 @@ extern "C" int32_t sparse_ffn_swiglu(void* hidden, int32_t n_rows, int32_t hidde
   g2.K = inter;
   g2.out_ld = hidden_size;
   g2.n_rows = n_rows;
-  if (launch_ffn_big<kModeResidual>(g2, hidden_size, k, (size_t)hidden_size * inter * 2, (size_t)k * inter * 2, s))
+  const size_t w2_bytes = (size_t)hidden_size * inter * 2, x2_bytes = (size_t)k * inter * 2;
+  constexpr int kResLds = kBigStages * (128 + 64) * kBigRowBytes;
+  if (launch_ffn_big<kModeResidual>(g2, hidden_size, k, w2_bytes, x2_bytes, s))
     ;
+  else if (w2_bytes < (size_t)INT_MAX && x2_bytes < (size_t)INT_MAX &&
+           big_lds_attr<ffn_big_kernel<kModeResidual, 2, 1, 2>>(kResLds))  // fewer rows: 128 x 64 tiles, 2 per CU
+    ffn_big_kernel<kModeResidual, 2, 1, 2><<<dim3(hidden_size / 128, cdiv(k, 64)), kFfnThreads, kResLds, s>>>(
+        g2, (uint32_t)w2_bytes, (uint32_t)x2_bytes);
   else if (small_grid(hidden_size / kRowsA, k))
     ffn_gemm_kernel<kModeResidual, 1><<<dim3(hidden_size / kRowsA, cdiv(k, 64)), kFfnThreads, 0, s>>>(g2);
   else
