@@ -627,6 +627,13 @@ __global__ __launch_bounds__(kFfnThreads, OCC) void qkv_big_kernel(QkvArgs a, ui
     for (int g4 = 0; g4 < 4; ++g4) {
       const int j = j0 + 8 * g4 + 4 * lg;
       float lo4[4], hi4[4];
+      // (cos, sin) of pairs j .. j + 3: two 16-byte loads (j is a multiple of 4)
+      float4 cs4[2] = {};
+      if (kind != 2) {
+        const float4* cp = reinterpret_cast<const float4*>(a.rope_cs + (size_t)m * half + j);
+        cs4[0] = cp[0];
+        cs4[1] = cp[1];
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float x = acc[0][y][4 * g4 + e], yv = acc[1][y][4 * g4 + e];
@@ -634,9 +641,10 @@ __global__ __launch_bounds__(kFfnThreads, OCC) void qkv_big_kernel(QkvArgs a, ui
           lo4[e] = x;
           hi4[e] = yv;
         } else {
-          const float2 cs = a.rope_cs[(size_t)m * half + j + e];
-          lo4[e] = x * cs.x - yv * cs.y;
-          hi4[e] = x * cs.y + yv * cs.x;
+          const float4 c = cs4[e >> 1];
+          const float cx = (e & 1) ? c.z : c.x, sy = (e & 1) ? c.w : c.y;
+          lo4[e] = x * cx - yv * sy;
+          hi4[e] = x * sy + yv * cx;
         }
       }
       if (kind == 2) {  // d-major page: element (d, slot) at d * P + slot
