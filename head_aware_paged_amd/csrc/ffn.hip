@@ -200,19 +200,23 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(FfnArgs a) {
   }
 }
 
-// ---- large-tile projection for launches of at least one work-group per CU ----
+// ---- large-tile projections: the LDS-ring main loop and its kernels ----
 //
-// Same products and epilogues as ffn_gemm_kernel, with the operand traffic of
-// LDS cut in half: each wave computes (32 WA) x (32 WB) outputs (accumulators
-// beyond the 256 architectural VGPRs live in AGPRs, so one wave per SIMD),
-// the work-group (64 WA) weight rows x (64 WB) token rows. K goes in 32-deep
-// slices through a ring of kBigStages LDS stages, filled by buffer loads with
-// the LDS destination (no register staging), each slice issued
-// kBigStages - 1 slices ahead. A stage row is 32 bf16 = four 16-byte chunks;
-// chunk c of row r sits at slot c ^ ((r / 4) % 4), so the 16-byte operand
-// reads of 16 consecutive rows fall in distinct bank groups. Token rows that
-// do not exist (past k, or an out-of-range index) read as zeros through the
-// buffer's range check.
+// Same products and epilogues as ffn_gemm_kernel. Each wave computes
+// (32 WA) x (32 WB) outputs, the work-group (64 WA) weight rows x (64 WB)
+// token rows. Each 16-byte LDS fragment feeds WB (A) or WA (B) MFMAs, so
+// the 4 x 4 tile of the sparse FFN reads LDS half as often per MFMA as the
+// 2 x 2 per-wave tile of ffn_gemm_kernel; its accumulators then exceed the
+// 256 architectural VGPRs and live in AGPRs (one wave per SIMD). Smaller
+// tiles (2 x 1, 2 x 2) serve launches with few token rows, two work-groups
+// per CU. K goes in 32-deep slices through a ring of kBigStages LDS stages,
+// filled by buffer loads with the LDS destination (no register staging),
+// each slice issued kBigStages - 1 slices ahead. A stage row is 32 bf16 =
+// four 16-byte chunks; chunk c of row r sits at slot c ^ ((r / 4) % 4), so
+// the 16-byte operand reads of 16 consecutive rows fall in distinct bank
+// groups. Rows that do not exist (token rows past k, an out-of-range index,
+// weight rows past the last head) read as zeros through the buffer's range
+// check.
 constexpr int kBigBK = 32;        // reduction depth per slice
 constexpr int kBigStages = 4;     // LDS ring depth
 constexpr int kBigRowBytes = kBigBK * 2;
@@ -410,13 +414,26 @@ __global__ __launch_bounds__(kFfnThreads, OCC) void ffn_big_kernel(FfnArgs a, ui
   }
 }
 
-// Dynamic LDS above the default limit is allowed once per kernel.
+// Dynamic LDS above the default limit, allowed once per kernel and device
+// (false: the caller takes its fallback kernel).
 template <auto* KERNEL>
 bool big_lds_attr(int bytes) {
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [bytes] { attr = hipFuncSetAttribute((const void*)KERNEL, hipFuncAttributeMaxDynamicSharedMemorySize, bytes); });
-  return attr == hipSuccess;
+  constexpr int kDevices = 64;
+  static std::mutex mu;
+  static signed char state[kDevices] = {};  // 0: not yet set, 1: set, -1: refused
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) {
+    (void)hipGetLastError();
+    return false;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (state[dev] == 0) {
+    state[dev] = hipFuncSetAttribute((const void*)KERNEL, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess
+                     ? 1
+                     : -1;
+    if (state[dev] < 0) (void)hipGetLastError();
+  }
+  return state[dev] > 0;
 }
 
 // The 256x256 large-tile path of the sparse FFN, when the launch has at least
