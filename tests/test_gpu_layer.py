@@ -102,6 +102,32 @@ def test_out_proj(n_rows, in_f, hd):
     _check_rounded("out_proj", bits(h), oracle.out_proj_residual(hidden, attn, w_o))
 
 
+def test_out_proj_operands_beyond_32bit_offsets():
+    """An attention input of more than 2^31 bytes (262,208 rows x 4,096 bf16):
+    past the 32-bit offsets of a buffer load, so the output projection takes
+    its general kernel; 16 sampled rows (both ends, the middle) against the
+    oracle, and every row outside the input left finite."""
+    n, in_f, hd = 262_208, 4096, 128
+    assert n * in_f * 2 > 2 ** 31
+    print(f"case out_proj n={n} in={in_f} hidden={hd} (> 2^31-byte input)", flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    attn = torch.randn(n, in_f, generator=gen, device="cuda").to(torch.bfloat16)
+    hidden = torch.randn(n, hd, generator=gen, device="cuda").to(torch.bfloat16)
+    w_o = (torch.randn(hd, in_f, generator=gen, device="cuda") * in_f ** -0.5).to(torch.bfloat16)
+    rows = np.array([0, 1, 63, 64, 1000, 65535, 131071, 131072, 200003, 262143, 262144, 262145, 262200, 262205,
+                     262206, 262207])
+    ri = torch.from_numpy(rows).cuda()
+    h0 = bits(hidden[ri])
+    a0 = bits(attn[ri])
+    from head_aware_paged_amd.session import SegPagedLayer
+    SegPagedLayer.out_proj_residual(attn, w_o, hidden)
+    torch.cuda.synchronize()
+    got = bits(hidden[ri])
+    _check_rounded("out_proj > 2^31 B", got, oracle.out_proj_residual(h0, a0, bits(w_o)))
+    assert bool(torch.isfinite(hidden.float()).all())
+
+
 @pytest.mark.parametrize("name", ["tiny_224", "retr_mixed", "mha_g1", "mistral_32k"])
 def test_layer_chain(name):
     w = workloads.mistral_32k() if name == "mistral_32k" else small(name)
