@@ -202,14 +202,14 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(FfnArgs a) {
 
 // ---- large-tile projections: the LDS-ring main loop and its kernels ----
 //
-// Same products and epilogues as ffn_gemm_kernel. Each wave computes
-// (32 WA) x (32 WB) outputs, the work-group (64 WA) weight rows x (64 WB)
-// token rows. Each 16-byte LDS fragment feeds WB (A) or WA (B) MFMAs, so
-// the 4 x 4 tile of the sparse FFN reads LDS half as often per MFMA as the
-// 2 x 2 per-wave tile of ffn_gemm_kernel; its accumulators then exceed the
-// 256 architectural VGPRs and live in AGPRs (one wave per SIMD). Smaller
-// tiles (2 x 1, 2 x 2) serve launches with few token rows, two work-groups
-// per CU. K goes in 32-deep slices through a ring of kBigStages LDS stages,
+// Same products and epilogues as ffn_gemm_kernel. A work-group has NA x NB
+// waves; each wave computes (32 WA) x (32 WB) outputs, the work-group
+// (NA 32 WA) weight rows x (NB 32 WB) token rows. Each 16-byte LDS fragment
+// feeds WB (A) or WA (B) MFMAs. The sparse FFN runs 8 waves (two per SIMD,
+// so one wave's MFMAs fill the matrix core while the other waits on LDS or a
+// barrier) on 256 x 256 and 128 x 256 tiles; the layer glue and launches
+// with few token rows run 4 waves on 128 x 128 and 128 x 64 tiles, two
+// work-groups per CU. K goes in 32-deep slices through a ring of kBigStages LDS stages,
 // filled by buffer loads with the LDS destination (no register staging),
 // each slice issued kBigStages - 1 slices ahead. A stage row is 32 bf16 =
 // four 16-byte chunks; chunk c of row r sits at slot c ^ ((r / 4) % 4), so
@@ -233,21 +233,38 @@ __device__ __forceinline__ u32x4 big_rsrc(const void* base, uint32_t bytes) {
 }
 __device__ __forceinline__ int big_swz(int row) { return (row >> 2) & 3; }
 
+// Tile shape: NA x NB waves, wave w in wave row w % NA (its 32 WA weight
+// rows) and wave column w / NA (its 32 WB token rows). A slice of a tile is
+// copied by 1 KiB DMA instructions of 16 rows each, IA (weight) and IB
+// (token) per wave.
+template <int WA, int WB, int NA, int NB>
+struct BigTile {
+  static constexpr int kWaves = NA * NB, kThreads = 64 * kWaves;
+  static constexpr int TA = NA * 32 * WA, TB = NB * 32 * WB;
+  static constexpr int IA = TA / kBigRowsPerDma / kWaves, IB = TB / kBigRowsPerDma / kWaves;
+  static_assert(IA * kBigRowsPerDma * kWaves == TA && IB * kBigRowsPerDma * kWaves == TB,
+                "every wave issues the same number of DMA instructions");
+  static constexpr int kLds = kBigStages * (TA + TB) * kBigRowBytes;
+};
+
 // Main loop of the large-tile path: acc[x][y] (wave block x of the A tile,
 // block y of the token tile) over K. For each of its DMA instructions (one
-// per 16-row group: A groups wave, wave + 4, ..., then the token groups alike)
-// the wave passes the source buffer and the byte offset at k = 0 of the
-// lane's 16-byte chunk (row (wave + 4 i) * 16 + lane / 4, chunk lane % 4 at
-// slot chunk ^ big_swz(row)); kBigOob reads a zero row.
-template <int WA, int WB>
-__device__ __forceinline__ void big_mainloop(const u32x4 (&ra)[WA], const int (&offa)[WA], const u32x4& rx,
-                                             const int (&offb)[WB], int K, char* lds, f32x16 (&acc)[WA][WB]) {
-  constexpr int TA = 64 * WA, TB = 64 * WB;
-  constexpr int STAGE = (TA + TB) * kBigRowBytes;
+// per 16-row group: A groups wave, wave + NA NB, ..., then the token groups
+// alike) the wave passes the source buffer and the byte offset at k = 0 of
+// the lane's 16-byte chunk (row (wave + NA NB i) * 16 + lane / 4, chunk
+// lane % 4 at slot chunk ^ big_swz(row)); kBigOob reads a zero row.
+template <int WA, int WB, int NA, int NB>
+__device__ __forceinline__ void big_mainloop(const u32x4 (&ra)[BigTile<WA, WB, NA, NB>::IA],
+                                             const int (&offa)[BigTile<WA, WB, NA, NB>::IA], const u32x4& rx,
+                                             const int (&offb)[BigTile<WA, WB, NA, NB>::IB], int K, char* lds,
+                                             f32x16 (&acc)[WA][WB]) {
+  using Tile = BigTile<WA, WB, NA, NB>;
+  constexpr int TA = Tile::TA, IA = Tile::IA, IB = Tile::IB, NW = Tile::kWaves;
+  constexpr int STAGE = (Tile::TA + Tile::TB) * kBigRowBytes;
   constexpr int KSTEPS = kBigBK / 16;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lrow = lane & 31, lg = lane >> 5;
-  const int wa = wave & 1, wb = wave >> 1;
+  const int wa = wave % NA, wb = wave / NA;
   const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   auto dma = [&](uint32_t lds_byte, const u32x4& rs, int off) __attribute__((always_inline)) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_byte), "v"(off), "s"(rs)
@@ -257,9 +274,9 @@ __device__ __forceinline__ void big_mainloop(const u32x4 (&ra)[WA], const int (&
     const uint32_t st = lds_base + (uint32_t)((sl % kBigStages) * STAGE);
     const int kb = sl * kBigRowBytes;
 #pragma unroll
-    for (int i = 0; i < WA; ++i) dma(st + (uint32_t)((wave + 4 * i) * 1024), ra[i], offa[i] + kb);
+    for (int i = 0; i < IA; ++i) dma(st + (uint32_t)((wave + NW * i) * 1024), ra[i], offa[i] + kb);
 #pragma unroll
-    for (int i = 0; i < WB; ++i) dma(st + (uint32_t)(TA * kBigRowBytes + (wave + 4 * i) * 1024), rx, offb[i] + kb);
+    for (int i = 0; i < IB; ++i) dma(st + (uint32_t)(TA * kBigRowBytes + (wave + NW * i) * 1024), rx, offb[i] + kb);
   };
 #pragma unroll
   for (int x = 0; x < WA; ++x)
@@ -272,7 +289,7 @@ __device__ __forceinline__ void big_mainloop(const u32x4 (&ra)[WA], const int (&
   auto rd = [&](const char* base, int row, int c) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x8*>(base + row * kBigRowBytes + 16 * (c ^ big_swz(row)));
   };
-  constexpr int kVm = (kBigStages - 2) * (WA + WB);  // this wave's DMA of the slices after the next
+  constexpr int kVm = (kBigStages - 2) * (IA + IB);  // this wave's DMA of the slices after the next
   static_assert(kVm < 64, "vmcnt immediate");
   for (int sl = 0; sl < nsl; ++sl) {
     // slice sl has landed for this wave (the kBigStages - 2 younger slices may
@@ -305,38 +322,40 @@ __device__ __forceinline__ void big_mainloop(const u32x4 (&ra)[WA], const int (&
   }
 }
 
-// Byte offset at k = 0 of this lane's chunk of token-tile DMA group i: token
-// row `row` of x (kBigOob when row < 0).
-template <int WB>
-__device__ __forceinline__ void big_token_offsets(int (&offb)[WB], int wave, int lane, int K,
-                                                  const int (&src)[WB]) {
+// Byte offset at k = 0 of this lane's chunk of token-tile DMA instruction i
+// (of IB, in a work-group of NW waves): token row src[i] of x (kBigOob when
+// src[i] < 0).
+template <int IB, int NW>
+__device__ __forceinline__ void big_token_offsets(int (&offb)[IB], int wave, int lane, int K,
+                                                  const int (&src)[IB]) {
 #pragma unroll
-  for (int i = 0; i < WB; ++i) {
-    const int row = (wave + 4 * i) * kBigRowsPerDma + lane / 4, slot = lane % 4;
+  for (int i = 0; i < IB; ++i) {
+    const int row = (wave + NW * i) * kBigRowsPerDma + lane / 4, slot = lane % 4;
     offb[i] = src[i] >= 0 ? (src[i] * K + 8 * (slot ^ big_swz(row))) * 2 : (int)kBigOob;
   }
 }
 
-// MODE kModeSwiglu: WA = 4; the A tile's 256 rows are gate rows f0 .. f0+63,
-// up rows f0 .. f0+63, gate rows f0+64 .., up rows f0+64 .. (64-row groups),
-// so wave wa holds gate blocks 0, 1 and the matching up blocks 2, 3 of
-// features f0 + 64 wa ... The work-group covers 128 features.
-// OCC: work-groups per CU the launch bounds allow (1 for the 256x256 tiles).
-template <int MODE, int WA, int WB, int OCC>
-__global__ __launch_bounds__(kFfnThreads, OCC) void ffn_big_kernel(FfnArgs a, uint32_t a_bytes, uint32_t x_bytes) {
-  constexpr int TA = 64 * WA, TB = 64 * WB;
-  static_assert(MODE != kModeSwiglu || WA == 4, "SwiGLU tile pairs gate and up blocks");
+// MODE kModeSwiglu: WA = 4, NA = 2; the A tile's 256 rows are gate rows
+// f0 .. f0+63, up rows f0 .. f0+63, gate rows f0+64 .., up rows f0+64 ..
+// (64-row groups), so wave row wa holds gate blocks 0, 1 and the matching up
+// blocks 2, 3 of features f0 + 64 wa ... The work-group covers 128 features.
+// OCC: work-groups per CU the launch bounds allow.
+template <int MODE, int WA, int WB, int NA, int NB, int OCC>
+__global__ __launch_bounds__(64 * NA * NB, OCC) void ffn_big_kernel(FfnArgs a, uint32_t a_bytes, uint32_t x_bytes) {
+  using Tile = BigTile<WA, WB, NA, NB>;
+  constexpr int TA = Tile::TA, TB = Tile::TB, IA = Tile::IA, IB = Tile::IB, NW = Tile::kWaves;
+  static_assert(MODE != kModeSwiglu || (WA == 4 && NA == 2), "SwiGLU tile pairs gate and up blocks");
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lrow = lane & 31, lg = lane >> 5;
-  const int wa = wave & 1, wb = wave >> 1;
+  const int wa = wave % NA, wb = wave / NA;
   const int f0 = blockIdx.x * (MODE == kModeSwiglu ? 128 : TA);  // first output feature
   const int m0 = blockIdx.y * TB;                                 // first token row
-  u32x4 ra[WA];
-  int offa[WA], offb[WB], srcb[WB];
+  u32x4 ra[IA];
+  int offa[IA], offb[IB], srcb[IB];
 #pragma unroll
-  for (int i = 0; i < WA; ++i) {
-    const int r0 = (wave + 4 * i) * kBigRowsPerDma, row = r0 + lane / 4, slot = lane % 4;
+  for (int i = 0; i < IA; ++i) {
+    const int r0 = (wave + NW * i) * kBigRowsPerDma, row = r0 + lane / 4, slot = lane % 4;
     int src;  // weight row of stage row `row`
     if (MODE == kModeSwiglu) {
       const int grp = r0 / 64;  // 0: gate, 1: up, 2: gate + 64, 3: up + 64 (uniform per instruction)
@@ -349,14 +368,14 @@ __global__ __launch_bounds__(kFfnThreads, OCC) void ffn_big_kernel(FfnArgs a, ui
     offa[i] = (src * a.K + 8 * (slot ^ big_swz(row))) * 2;
   }
 #pragma unroll
-  for (int i = 0; i < WB; ++i) {
-    const int m = m0 + (wave + 4 * i) * kBigRowsPerDma + lane / 4;
+  for (int i = 0; i < IB; ++i) {
+    const int m = m0 + (wave + NW * i) * kBigRowsPerDma + lane / 4;
     const int src = m < a.k_tokens ? (MODE == kModeSwiglu ? a.idx[m] : m) : -1;
     srcb[i] = src >= 0 && (MODE != kModeSwiglu || src < a.n_rows) ? src : -1;
   }
-  big_token_offsets<WB>(offb, wave, lane, a.K, srcb);
+  big_token_offsets<IB, NW>(offb, wave, lane, a.K, srcb);
   f32x16 acc[WA][WB];
-  big_mainloop<WA, WB>(ra, offa, big_rsrc(a.x, x_bytes), offb, a.K, lds, acc);
+  big_mainloop<WA, WB, NA, NB>(ra, offa, big_rsrc(a.x, x_bytes), offb, a.K, lds, acc);
 
   // lane holds token row m0 + 32 (WB wb + y) + lrow and features 8 (i/4) + 4 lg + i%4 of each block
 #pragma unroll
@@ -436,20 +455,23 @@ bool big_lds_attr(int bytes) {
   return state[dev] > 0;
 }
 
-// The 256x256 large-tile path of the sparse FFN, when the launch has at least
+// The 8-wave large-tile path of the sparse FFN (SwiGLU: 256 weight rows =
+// 128 features x 256 token rows, 128 x 64 per wave; down projection: 128
+// features x 256 token rows, 64 x 64 per wave), when the launch has at least
 // one work-group per CU and every buffer fits the 32-bit offsets of a buffer
-// load; returns false to let the caller take the general kernel.
+// load; returns false to let the caller take another kernel.
 template <int MODE>
 bool launch_ffn_big(const FfnArgs& g, int n_features, int rows, size_t a_bytes, size_t x_bytes, hipStream_t s) {
-  constexpr int WA = MODE == kModeSwiglu ? 4 : 2, WB = 4;
-  constexpr int TB = 64 * WB, FEAT = MODE == kModeSwiglu ? 128 : 64 * WA;
-  constexpr int LDS = kBigStages * (64 * WA + TB) * kBigRowBytes;
+  constexpr int WA = MODE == kModeSwiglu ? 4 : 2, WB = 2, NA = 2, NB = 4;
+  using Tile = BigTile<WA, WB, NA, NB>;
+  constexpr int FEAT = MODE == kModeSwiglu ? 128 : Tile::TA;
   if (g.K % kBigBK != 0 || n_features % FEAT != 0) return false;
   if (a_bytes >= (size_t)INT_MAX || x_bytes >= (size_t)INT_MAX) return false;
-  const dim3 grid(n_features / FEAT, cdiv(rows, TB));
+  const dim3 grid(n_features / FEAT, cdiv(rows, Tile::TB));
   if ((int64_t)grid.x * grid.y < 256) return false;
-  if (!big_lds_attr<ffn_big_kernel<MODE, WA, WB, 1>>(LDS)) return false;
-  ffn_big_kernel<MODE, WA, WB, 1><<<grid, kFfnThreads, LDS, s>>>(g, (uint32_t)a_bytes, (uint32_t)x_bytes);
+  if (!big_lds_attr<ffn_big_kernel<MODE, WA, WB, NA, NB, 1>>(Tile::kLds)) return false;
+  ffn_big_kernel<MODE, WA, WB, NA, NB, 1><<<grid, Tile::kThreads, Tile::kLds, s>>>(g, (uint32_t)a_bytes,
+                                                                                   (uint32_t)x_bytes);
   return true;
 }
 
@@ -624,9 +646,9 @@ __global__ __launch_bounds__(kFfnThreads, OCC) void qkv_big_kernel(QkvArgs a, ui
     const int m = m0 + (wave + 4 * i) * kBigRowsPerDma + lane / 4;
     srcb[i] = m < a.T ? m : -1;
   }
-  big_token_offsets<WB>(offb, wave, lane, a.K, srcb);
+  big_token_offsets<WB, 4>(offb, wave, lane, a.K, srcb);
   f32x16 acc[WA][WB];
-  big_mainloop<WA, WB>(ra, offa, big_rsrc(a.x, x_bytes), offb, a.K, lds, acc);
+  big_mainloop<WA, WB, 2, 2>(ra, offa, big_rsrc(a.x, x_bytes), offb, a.K, lds, acc);
 
   // acc[0][y][i] and acc[1][y][i]: dims j and j + D/2 of head `head`, token
   // row m = m0 + 32 (WB wb + y) + lrow, with j = j0 + 8 (i/4) + 4 lg + i%4
@@ -739,12 +761,12 @@ extern "C" int32_t sparse_ffn_swiglu(void* hidden, int32_t n_rows, int32_t hidde
   g2.out_ld = hidden_size;
   g2.n_rows = n_rows;
   const size_t w2_bytes = (size_t)hidden_size * inter * 2, x2_bytes = (size_t)k * inter * 2;
-  constexpr int kResLds = kBigStages * (128 + 64) * kBigRowBytes;
+  constexpr int kResLds = BigTile<2, 1, 2, 2>::kLds;
   if (launch_ffn_big<kModeResidual>(g2, hidden_size, k, w2_bytes, x2_bytes, s))
     ;
   else if (w2_bytes < (size_t)INT_MAX && x2_bytes < (size_t)INT_MAX &&
-           big_lds_attr<ffn_big_kernel<kModeResidual, 2, 1, 2>>(kResLds))  // fewer rows: 128 x 64 tiles, 2 per CU
-    ffn_big_kernel<kModeResidual, 2, 1, 2><<<dim3(hidden_size / 128, cdiv(k, 64)), kFfnThreads, kResLds, s>>>(
+           big_lds_attr<ffn_big_kernel<kModeResidual, 2, 1, 2, 2, 2>>(kResLds))  // fewer rows: 128 x 64, 2 per CU
+    ffn_big_kernel<kModeResidual, 2, 1, 2, 2, 2><<<dim3(hidden_size / 128, cdiv(k, 64)), kFfnThreads, kResLds, s>>>(
         g2, (uint32_t)w2_bytes, (uint32_t)x2_bytes);
   else if (small_grid(hidden_size / kRowsA, k))
     ffn_gemm_kernel<kModeResidual, 1><<<dim3(hidden_size / kRowsA, cdiv(k, 64)), kFfnThreads, 0, s>>>(g2);
@@ -831,7 +853,7 @@ extern "C" int32_t segkv_qkv_rope_append(const segkv_dims* dims, const segkv_met
   a.D = D;
   const int nx = cdiv((Hq + 2 * Hkv) * D, kRowsA);
   const size_t w_bytes = (size_t)(Hq + 2 * Hkv) * D * hidden_size * 2, x_bytes = (size_t)T * hidden_size * 2;
-  constexpr int kQkvWB = 2, kQkvLds = kBigStages * (128 + 64 * kQkvWB) * kBigRowBytes;
+  constexpr int kQkvWB = 2, kQkvLds = BigTile<2, kQkvWB, 2, 2>::kLds;
   if (hidden_size % kBigBK == 0 && w_bytes < (size_t)INT_MAX && x_bytes < (size_t)INT_MAX &&
       big_lds_attr<qkv_big_kernel<kQkvWB, 2>>(kQkvLds))
     qkv_big_kernel<kQkvWB, 2><<<dim3(nx, cdiv((int)T, 64 * kQkvWB)), kFfnThreads, kQkvLds, s>>>(
@@ -870,10 +892,11 @@ extern "C" int32_t segkv_out_proj_residual(const void* attn, int32_t n_rows, int
   // tile as the 64-row-token form of ffn_gemm_kernel, which stays for
   // operands beyond 32-bit buffer offsets)
   const size_t w_bytes = (size_t)hidden_size * in_features * 2, x_bytes = (size_t)n_rows * in_features * 2;
-  constexpr int kOpLds = kBigStages * (128 + 64) * kBigRowBytes;
-  if (w_bytes < (size_t)INT_MAX && x_bytes < (size_t)INT_MAX && big_lds_attr<ffn_big_kernel<kModeResidual, 2, 1, 2>>(kOpLds))
-    ffn_big_kernel<kModeResidual, 2, 1, 2><<<dim3(nx, cdiv(n_rows, 64)), kFfnThreads, kOpLds, hipStream_t(stream)>>>(
-        g, (uint32_t)w_bytes, (uint32_t)x_bytes);
+  constexpr int kOpLds = BigTile<2, 1, 2, 2>::kLds;
+  if (w_bytes < (size_t)INT_MAX && x_bytes < (size_t)INT_MAX &&
+      big_lds_attr<ffn_big_kernel<kModeResidual, 2, 1, 2, 2, 2>>(kOpLds))
+    ffn_big_kernel<kModeResidual, 2, 1, 2, 2, 2><<<dim3(nx, cdiv(n_rows, 64)), kFfnThreads, kOpLds,
+                                                   hipStream_t(stream)>>>(g, (uint32_t)w_bytes, (uint32_t)x_bytes);
   else if (small_grid(nx, n_rows))
     ffn_gemm_kernel<kModeResidual, 1><<<dim3(nx, cdiv(n_rows, 64)), kFfnThreads, 0, hipStream_t(stream)>>>(g);
   else

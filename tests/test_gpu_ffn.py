@@ -74,3 +74,14 @@ def test_full_8k_all_selected_rows():
     idx = np.sort(np.random.default_rng(1).choice(8192, size=2048, replace=False)).astype(np.int32)
     got = run_ffn(d, idx)
     check(d, idx, got)
+
+
+def test_8k_ragged_row_count():
+    """k = 1800 selected rows at 8K: the large-tile kernels' last token tile is
+    partly past k (rows read as zeros, no output written for them)."""
+    w = workloads.sparse_ffn_8k()
+    print("case sparse_ffn_8k: FFN on 1800 selected rows", flush=True)
+    d = dict(hidden=w.hidden, w_gate=w.w_gate, w_up=w.w_up, w_down=w.w_down)
+    idx = np.sort(np.random.default_rng(7).choice(8192, size=1800, replace=False)).astype(np.int32)
+    got = run_ffn(d, idx)
+    check(d, idx, got)
