@@ -647,32 +647,45 @@ __global__ __launch_bounds__(kFfnThreads, OCC) void qkv_big_kernel(QkvArgs a, ui
     srcb[i] = m < a.T ? m : -1;
   }
   big_token_offsets<WB, 4>(offb, wave, lane, a.K, srcb);
-  f32x16 acc[WA][WB];
-  big_mainloop<WA, WB, 2, 2>(ra, offa, big_rsrc(a.x, x_bytes), offb, a.K, lds, acc);
 
   // acc[0][y][i] and acc[1][y][i]: dims j and j + D/2 of head `head`, token
-  // row m = m0 + 32 (WB wb + y) + lrow, with j = j0 + 8 (i/4) + 4 lg + i%4
+  // row m = m0 + 32 (WB wb + y) + lrow, with j = j0 + 8 (i/4) + 4 lg + i%4.
+  // The epilogue's page slots and (cos, sin) pairs are loaded before the
+  // main loop, so they do not add a memory round trip at its end.
   const int head = (n0 + 64 * wa) / a.D, j0 = a.D == 128 ? 32 * wa : 0, half = a.D / 2;
-  if (head >= a.Hq + 2 * a.Hkv) return;  // the unused half of the last tile
+  const bool head_ok = head < a.Hq + 2 * a.Hkv;  // false: the unused half of the last tile
   const int kind = head < a.Hq ? 0 : head < a.Hq + a.Hkv ? 1 : 2;  // Q, K, V
   const int hk = kind == 1 ? head - a.Hq : head - a.Hq - a.Hkv;
+  int slot[WB];
+  float4 cs[WB][4][2];  // (cos, sin) of pairs j .. j + 3 per g4: two 16-byte loads (j is a multiple of 4)
 #pragma unroll
   for (int y = 0; y < WB; ++y) {
     const int m = m0 + 32 * (WB * wb + y) + lrow;
-    if (m >= a.T) continue;
-    const int slot = kind == 0 ? 0 : a.row_slot[(size_t)m * a.Hkv + hk];
-    if (slot < 0) continue;  // no page for this row: nothing written
+    const bool row_ok = head_ok && m < a.T;
+    slot[y] = row_ok && kind != 0 ? a.row_slot[(size_t)m * a.Hkv + hk] : 0;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      cs[y][g4][0] = cs[y][g4][1] = float4{0.f, 0.f, 0.f, 0.f};
+      if (row_ok && kind != 2) {
+        const float4* cp = reinterpret_cast<const float4*>(a.rope_cs + (size_t)m * half + j0 + 8 * g4 + 4 * lg);
+        cs[y][g4][0] = cp[0];
+        cs[y][g4][1] = cp[1];
+      }
+    }
+  }
+  f32x16 acc[WA][WB];
+  big_mainloop<WA, WB, 2, 2>(ra, offa, big_rsrc(a.x, x_bytes), offb, a.K, lds, acc);
+
+  if (!head_ok) return;
+#pragma unroll
+  for (int y = 0; y < WB; ++y) {
+    const int m = m0 + 32 * (WB * wb + y) + lrow;
+    if (m >= a.T || slot[y] < 0) continue;  // no page for this row: nothing written
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int j = j0 + 8 * g4 + 4 * lg;
       float lo4[4], hi4[4];
-      // (cos, sin) of pairs j .. j + 3: two 16-byte loads (j is a multiple of 4)
-      float4 cs4[2] = {};
-      if (kind != 2) {
-        const float4* cp = reinterpret_cast<const float4*>(a.rope_cs + (size_t)m * half + j);
-        cs4[0] = cp[0];
-        cs4[1] = cp[1];
-      }
+      const float4 (&cs4)[2] = cs[y][g4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float x = acc[0][y][4 * g4 + e], yv = acc[1][y][4 * g4 + e];
@@ -687,14 +700,14 @@ __global__ __launch_bounds__(kFfnThreads, OCC) void qkv_big_kernel(QkvArgs a, ui
         }
       }
       if (kind == 2) {  // d-major page: element (d, slot) at d * P + slot
-        uint16_t* vp = a.v_pool + (size_t)(slot / kPage) * a.D * kPage + slot % kPage;
+        uint16_t* vp = a.v_pool + (size_t)(slot[y] / kPage) * a.D * kPage + slot[y] % kPage;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           vp[(size_t)(j + e) * kPage] = float_to_bf16_bits(lo4[e]);
           vp[(size_t)(j + e + half) * kPage] = float_to_bf16_bits(hi4[e]);
         }
       } else {
-        uint16_t* dst = kind == 0 ? a.q_out + ((size_t)m * a.Hq + head) * a.D : a.k_pool + (size_t)slot * a.D;
+        uint16_t* dst = kind == 0 ? a.q_out + ((size_t)m * a.Hq + head) * a.D : a.k_pool + (size_t)slot[y] * a.D;
         const u32x2 wl = {(uint32_t)float_to_bf16_bits(lo4[0]) | (uint32_t)float_to_bf16_bits(lo4[1]) << 16,
                           (uint32_t)float_to_bf16_bits(lo4[2]) | (uint32_t)float_to_bf16_bits(lo4[3]) << 16};
         const u32x2 wh = {(uint32_t)float_to_bf16_bits(hi4[0]) | (uint32_t)float_to_bf16_bits(hi4[1]) << 16,
