@@ -296,6 +296,7 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kTopkSub = 256;  // keys per wave sub-block (64 lanes x 4)
 constexpr int kTopkMaxRegSub = 15;  // register-resident up to 15 x 256 x 16 = 61440 keys (no spills)
+constexpr int kTopkSplitLoad = 12;  // sub-blocks up to which all key loads precede their ordering
 constexpr int kTopkHist = 256 * 64;  // words of one histogram buffer
 constexpr int kTopkSegSub = 9;       // up to 9 sub-blocks per wave, every wave's selection fits its own LDS segment
 constexpr int kTopkLdsWords = kTopkWaves * kTopkSub * kTopkSegSub + 64;  // >= both histogram buffers
@@ -316,8 +317,9 @@ __device__ __forceinline__ uint32_t ordered_bits(uint32_t b) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Keys 4 lane + e of sub-block u; positions past n read as 0, below every real key.
-__device__ __forceinline__ u32x4 topk_load4(const uint32_t* bits, int j, int n, bool vec) {
+// Keys j .. j + 3 (4 lane + e of a sub-block): the raw fp32 bits, then their
+// ordered form; positions past n read as 0, below every real key.
+__device__ __forceinline__ u32x4 topk_load_raw4(const uint32_t* bits, int j, int n, bool vec) {
   u32x4 x;
   if (vec && j + 3 < n) {
     x = *reinterpret_cast<const u32x4*>(bits + j);
@@ -327,12 +329,18 @@ __device__ __forceinline__ u32x4 topk_load4(const uint32_t* bits, int j, int n, 
     x[2] = j + 2 < n ? bits[j + 2] : 0u;
     x[3] = j + 3 < n ? bits[j + 3] : 0u;
   }
+  return x;
+}
+__device__ __forceinline__ u32x4 topk_order4(const u32x4& x, int j, int n) {
   u32x4 o;
   o[0] = j < n ? ordered_bits(x[0]) : 0u;
   o[1] = j + 1 < n ? ordered_bits(x[1]) : 0u;
   o[2] = j + 2 < n ? ordered_bits(x[2]) : 0u;
   o[3] = j + 3 < n ? ordered_bits(x[3]) : 0u;
   return o;
+}
+__device__ __forceinline__ u32x4 topk_load4(const uint32_t* bits, int j, int n, bool vec) {
+  return topk_order4(topk_load_raw4(bits, j, n, vec), j, n);
 }
 
 // Lanes below this one whose bit is set in m, plus acc.
@@ -370,8 +378,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   const int base = wave * ns * kTopkSub + 4 * lane;
   const uint32_t* bits = reinterpret_cast<const uint32_t*>(scores);
   const bool vec = (reinterpret_cast<uintptr_t>(bits) & 15) == 0;
+  // Up to kTopkSplitLoad sub-blocks, the key loads are issued first, one
+  // 16-byte load per lane and sub-block wherever the 4 keys lie inside the
+  // vector (no branch between them, so no load waits for another); both
+  // histogram buffers are cleared while they are in flight. Then a partial
+  // last quad (or a vector that is not 16-byte aligned) is read key by key,
+  // and the keys take their ordered form. With more sub-blocks the fix-up's
+  // registers would spill, so each quad is loaded and ordered at once.
+  constexpr bool kSplit = S > 0 && S <= kTopkSplitLoad;
   u32x4 reg[SR];
-  if constexpr (S > 0) {
+  if constexpr (kSplit) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const int j = base + kTopkSub * u;
+      reg[u] = u32x4{0, 0, 0, 0};
+      if (vec && j + 3 < n) reg[u] = *reinterpret_cast<const u32x4*>(bits + j);
+    }
+  } else if constexpr (S > 0) {
 #pragma unroll
     for (int u = 0; u < S; ++u) reg[u] = topk_load4(bits, base + kTopkSub * u, n, vec);
   }
@@ -383,6 +406,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   char* const hbytes = reinterpret_cast<char*>(hist);
 #pragma unroll
   for (int x = tid; x < 2 * kTopkHist / 4; x += kTopkThreads) reinterpret_cast<u32x4*>(hist)[x] = u32x4{0, 0, 0, 0};
+  if constexpr (kSplit) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const int j = base + kTopkSub * u;
+      if (!(vec && j + 3 < n) && j < n) reg[u] = topk_load_raw4(bits, j, n, false);
+      reg[u] = topk_order4(reg[u], j, n);
+    }
+  }
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < (S > 0 ? S : ns); ++u) {
