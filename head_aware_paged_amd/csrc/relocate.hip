@@ -8,15 +8,10 @@
 // a key by delta positions rotates pair (j, j + D/2) by delta * omega_j.
 //
 // Bandwidth-bound: every move reads and writes one K page (and one V page).
-// A 256-thread work-group takes a batch of 2 (D = 128) or 4 (D = 64) moves,
-// 16 KiB of K and V. The chunks a wave copies always lie in one move, so the
-// page ids come in by scalar loads with no barrier before the page loads; all 16-byte
-// loads of the batch are issued first (V, then K), the batch's cos/sin table
-// (angle reduced in fp64, cos/sin in fp32, in LDS) is computed while they fly,
-// V is stored as soon as it lands, then K is rotated and stored. Pages are
-// read once and written once, so loads and stores are non-temporal (on random
-// 4 KiB pages this gets within a few per cent of a plain copy of the same
-// pages).
+// A work-group takes a batch of 1 (D = 128) or 2 (D = 64) moves, so that a
+// layer's few thousand moves spread over many work-groups per CU; it keeps all
+// 16-byte loads of the batch in flight and computes the batch's cos/sin table
+// (angle reduced in fp64, cos/sin in fp32, in LDS) while they fly.
 #include <cmath>
 
 #include "common.h"
@@ -26,9 +21,9 @@ namespace {
 
 SEGKV_DEVICE_FLAG(g_reloc_check);  // bit 1: a move's source or destination page outside its pool
 
-constexpr int kRelocThreads = 256;
+constexpr int kRelocThreads = 128;
 template <int D>
-constexpr int moves_per_batch() { return D == 128 ? 2 : 4; }
+constexpr int moves_per_batch() { return D == 128 ? 1 : 2; }
 
 template <int D>
 __global__ __launch_bounds__(kRelocThreads) void relocate_kernel(
@@ -39,58 +34,53 @@ __global__ __launch_bounds__(kRelocThreads) void relocate_kernel(
   constexpr int kHalf = D / 2;
   constexpr int kChunksPerHalf = kHalf / 8;          // 16-byte chunks in one half row
   constexpr int kPairsPerPage = kPage * kChunksPerHalf;
-  constexpr int kVChunksPerPage = kPage * D / 8;
-  constexpr int kKPerThread = kMovesPerBatch * kPairsPerPage / kRelocThreads;
-  constexpr int kVPerThread = kMovesPerBatch * kVChunksPerPage / kRelocThreads;
-  static_assert(kKPerThread * kRelocThreads == kMovesPerBatch * kPairsPerPage &&
-                kVPerThread * kRelocThreads == kMovesPerBatch * kVChunksPerPage, "batch shape");
-  static_assert(kPairsPerPage % 64 == 0 && kVChunksPerPage % 64 == 0, "a wave's chunks must lie in one move");
+  constexpr int kKPairs = kMovesPerBatch * kPairsPerPage;
+  constexpr int kKPerThread = kKPairs / kRelocThreads;
+  constexpr int kVChunks = kMovesPerBatch * kPage * D / 8;
+  constexpr int kVPerThread = kVChunks / kRelocThreads;
+  static_assert(kKPairs % kRelocThreads == 0 && kVChunks % kRelocThreads == 0, "batch shape");
 
   __shared__ double inv_freq[kHalf];
   __shared__ float cs[kMovesPerBatch][kHalf][2];
+  __shared__ int s_src[kMovesPerBatch], s_dst[kMovesPerBatch], s_ok[kMovesPerBatch], s_delta[kMovesPerBatch];
 
   const int tid = threadIdx.x;
   const int m0 = blockIdx.x * kMovesPerBatch;
-  // the move of a wave's chunk, its page ids (scalar loads) and whether both ids are in range
-  auto move_of = [&](int b, int& s, int& d) {
-    const int m = m0 + b;
-    s = -1;
-    d = -1;
+  if (tid < kMovesPerBatch) {
+    const int m = m0 + tid;
+    int s = -1, d = -1, ok = 0, dl = 0;
     if (m < n_moves) {
-      const int s_ = src_page[m], d_ = dst_page[m];
-      const bool ok = s_ >= 0 && s_ < src_pages && d_ >= 0 && d_ < dst_pages;
+      s = src_page[m];
+      d = dst_page[m];
+      dl = delta[m];
+      ok = (s >= 0 && s < src_pages && d >= 0 && d < dst_pages) ? 1 : 0;
       SEGKV_DCHECK(g_reloc_check, ok, 1);
-      if (ok) {
-        s = s_;
-        d = d_;
-      }
     }
-  };
+    s_src[tid] = s;
+    s_dst[tid] = d;
+    s_ok[tid] = ok;
+    s_delta[tid] = dl;
+  }
+  __syncthreads();
+  // issue every load of the batch first; the cos/sin table is computed while they fly
   u32x4 kx[kKPerThread], ky[kKPerThread], vv[kVPerThread];
-  int kd[kKPerThread], vd[kVPerThread];
+#pragma unroll
+  for (int u = 0; u < kKPerThread; ++u) {
+    const int q = tid + u * kRelocThreads;
+    const int b = q / kPairsPerPage, w = q % kPairsPerPage;
+    const int t = w / kChunksPerHalf, c = w % kChunksPerHalf;
+    if (s_ok[b]) {
+      const u32x4* row = reinterpret_cast<const u32x4*>(k_src + ((size_t)s_src[b] * kPage + t) * D);
+      kx[u] = __builtin_nontemporal_load(row + c);  // the cached segment is read once
+      ky[u] = __builtin_nontemporal_load(row + c + kChunksPerHalf);
+    }
+  }
   if (v_src != nullptr) {
 #pragma unroll
     for (int u = 0; u < kVPerThread; ++u) {
       const int q = tid + u * kRelocThreads;
-      int s_, d_;
-      move_of(__builtin_amdgcn_readfirstlane(q / kVChunksPerPage), s_, d_);
-      vd[u] = d_;
-      if (s_ >= 0)
-        vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_src + (size_t)s_ * kPage * D) +
-                                           q % kVChunksPerPage);  // the cached segment is read once
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kKPerThread; ++u) {
-    const int q = tid + u * kRelocThreads;
-    const int w = q % kPairsPerPage, t = w / kChunksPerHalf, c = w % kChunksPerHalf;
-    int s_, d_;
-    move_of(__builtin_amdgcn_readfirstlane(q / kPairsPerPage), s_, d_);
-    kd[u] = d_;
-    if (s_ >= 0) {
-      const u32x4* row = reinterpret_cast<const u32x4*>(k_src + ((size_t)s_ * kPage + t) * D);
-      kx[u] = __builtin_nontemporal_load(row + c);
-      ky[u] = __builtin_nontemporal_load(row + c + kChunksPerHalf);
+      const int b = q / (kPage * D / 8), w = q % (kPage * D / 8);
+      if (s_ok[b]) vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_src + (size_t)s_src[b] * kPage * D) + w);
     }
   }
   if (tid < kHalf) inv_freq[tid] = exp2(-2.0 * (double)tid / (double)D * log2_theta);
@@ -98,25 +88,18 @@ __global__ __launch_bounds__(kRelocThreads) void relocate_kernel(
   for (int e = tid; e < kMovesPerBatch * kHalf; e += kRelocThreads) {
     const int b = e / kHalf, j = e % kHalf;
     float sn = 0.f, cn = 1.f;
-    if (m0 + b < n_moves) {
+    if (s_ok[b]) {
       // angle in fp64, reduced to [-pi, pi] in fp64 by Cody-Waite reduction
       // (x - n C1 - n C2 with 2 pi = C1 + C2, C1 the fp64 value of 2 pi and C2
       // its remainder), then cos/sin in fp32
-      const double ang = (double)delta[m0 + b] * inv_freq[j];
+      const double ang = (double)s_delta[b] * inv_freq[j];
       const double n = rint(ang * 0.15915494309189535);
       sincosf((float)fma(-n, 2.4492935982947064e-16, fma(-n, 6.283185307179586, ang)), &sn, &cn);
     }
     cs[b][j][0] = cn;
     cs[b][j][1] = sn;
   }
-  if (v_src != nullptr) {
-#pragma unroll
-    for (int u = 0; u < kVPerThread; ++u) {
-      const int q = tid + u * kRelocThreads;
-      if (vd[u] >= 0)
-        __builtin_nontemporal_store(vv[u], reinterpret_cast<u32x4*>(v_dst + (size_t)vd[u] * kPage * D) + q % kVChunksPerPage);
-    }
-  }
+
   __syncthreads();
 
 #pragma unroll
@@ -124,7 +107,7 @@ __global__ __launch_bounds__(kRelocThreads) void relocate_kernel(
     const int q = tid + u * kRelocThreads;
     const int b = q / kPairsPerPage, w = q % kPairsPerPage;
     const int t = w / kChunksPerHalf, c = w % kChunksPerHalf;
-    if (kd[u] < 0) continue;
+    if (!s_ok[b]) continue;
     u32x4 ox, oy;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -143,9 +126,17 @@ __global__ __launch_bounds__(kRelocThreads) void relocate_kernel(
       ox[e] = outx;
       oy[e] = outy;
     }
-    u32x4* row = reinterpret_cast<u32x4*>(k_dst + ((size_t)kd[u] * kPage + t) * D);
-    __builtin_nontemporal_store(ox, row + c);
-    __builtin_nontemporal_store(oy, row + c + kChunksPerHalf);
+    u32x4* row = reinterpret_cast<u32x4*>(k_dst + ((size_t)s_dst[b] * kPage + t) * D);
+    row[c] = ox;
+    row[c + kChunksPerHalf] = oy;
+  }
+  if (v_src != nullptr) {
+#pragma unroll
+    for (int u = 0; u < kVPerThread; ++u) {
+      const int q = tid + u * kRelocThreads;
+      const int b = q / (kPage * D / 8), w = q % (kPage * D / 8);
+      if (s_ok[b]) reinterpret_cast<u32x4*>(v_dst + (size_t)s_dst[b] * kPage * D)[w] = vv[u];
+    }
   }
 }
 
