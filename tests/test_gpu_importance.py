@@ -108,6 +108,21 @@ def test_many_requests():
     check(w, imp, idx, 16, k)
 
 
+def test_requests_beyond_one_topk_launch():
+    """70 requests x 2 kv heads: the selections take two top-k launches (64
+    vectors per launch), the second with its own score and output offsets."""
+    nreq = 70
+    w = workloads.make_custom("many_req_70", Hq=4, Hkv=2, D=64, theta=1e4,
+                              seg_lens_per_req=[[32 + 16 * (r % 3), 17 + 5 * (r % 7)] for r in range(nreq)],
+                              orig_starts_per_req=[[5 * r, None] for r in range(nreq)],
+                              classes=[(G_, L_, D_)[(r + h) % 3] for r in range(nreq) for h in range(2)],
+                              windows=[(0, 20, 0)[(r + h) % 3] for r in range(nreq) for h in range(2)])
+    print("case many_req_70: importance + top-k, 70 requests, n_last 8", flush=True)
+    k = [(r * 5) % 30 for r in range(nreq)]
+    imp, idx = run(w, 8, k)
+    check(w, imp, idx, 8, k)
+
+
 @pytest.mark.parametrize("n,k,levels", [(1000, 100, 7), (33280, 8320, 50), (4096, 4096, 3), (5, 1, 1),
                                         (70000, 1, 0), (2049, 2048, 2), (4097, 100, 0), (61440, 30000, 0),
                                         (61441, 5, 0), (70000, 35000, 1000), (36864, 36863, 1),
