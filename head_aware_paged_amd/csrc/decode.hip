@@ -185,15 +185,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_main_kernel(DecArgs a) {
   }
 }
 
-// Work-group (request, query head, 32-dim slice of the head): merges the runs
+// Work-group (request, query head, 16-dim slice of the head): merges the runs
 // of its kv head's table and the new token:
 //   m* = max(m_new, max_c m_c), L = 2^(m_new - m*) + sum_c 2^(m_c - m*) l_c,
 //   O = (2^(m_new - m*) v_new + sum_c 2^(m_c - m*) O_c) / L, LSE = (m* + log2 L) ln 2,
-// with m_new = scale log2(e) q . k_new. Thread (d, q) adds runs q, q + 32, ...
+// with m_new = scale log2(e) q . k_new. Thread (d, q) adds runs q, q + 64, ...
 // into four accumulators (loads of four runs in flight); the partial sums are
 // combined in a fixed order, so the result does not depend on timing.
 constexpr int kDecCombThreads = 1024;
-constexpr int kDecCombDims = 32;                                // dims per work-group
+constexpr int kDecCombDims = 16;                                // dims per work-group
 constexpr int kDecCombGroups = kDecCombThreads / kDecCombDims;  // run groups
 
 __device__ __forceinline__ float dec_wave_sum(float x) {
