@@ -21,9 +21,9 @@ namespace {
 
 SEGKV_DEVICE_FLAG(g_dec_check);  // bit 1: a table page id outside the pool
 
-constexpr int kDecThreads = 256;
+constexpr int kDecThreads = 512;
 constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kDecPagesPerWave = 2;
+constexpr int kDecPagesPerWave = 1;
 constexpr int kDecChunk = kDecWaves * kDecPagesPerWave;  // table entries per work-group
 constexpr int kDecMaxG = 16;                             // query heads per kv head (MFMA columns)
 constexpr float kDecLog2e = 1.4426950408889634f;
@@ -57,8 +57,9 @@ __device__ __forceinline__ bool dec_visible(const HeadView& v, int j) {
   return true;
 }
 
-// Work-group (run c of the table of pair k): wave w takes entries
-// 8 c + 2 w and 8 c + 2 w + 1. Per page, S = K Q^T on the 16x16x32 MFMA
+// Work-group (run c of the table of pair k): wave w of the 8 takes entry
+// 8 c + w, so each wave's page loads are all in flight at once and the
+// run's eight pages arrive together. Per page, S = K Q^T on the 16x16x32 MFMA
 // (A: 16 keys x 32 dims of the token-major K page; B: the G query rows,
 // columns G..15 zero), so lane l holds S[key 4 (l / 16) + i][head l % 16];
 // that is exactly the A operand of the 16x16x16 PV product (rows = heads,
