@@ -14,6 +14,8 @@
 #include <climits>
 #include <mutex>
 
+#include <cmath>
+
 #include "common.h"
 #include "plan.h"
 
@@ -499,7 +501,7 @@ struct QkvRowArgs {
   int32_t* row_slot;   // [T][Hkv] page * P + slot of row t's K/V for kv head h, or -1
   int R, T, Hkv, D;
   int64_t pool_pages;
-  double theta;
+  double log2_theta;  // log2 of the RoPE base, taken on the host
 };
 
 // One work-group per query row: its request (largest r with cu_q[r] <= t), its
@@ -515,7 +517,7 @@ __global__ __launch_bounds__(kRowThreads) void qkv_rows_kernel(QkvRowArgs a) {
   const int r = lo, sq = a.seg_indptr[r + 1] - 1, tl = t - a.cu_q[r];
   const int pos = a.seg_start[sq] + tl;
   for (int j = tid; j < a.D / 2; j += kRowThreads) {
-    const double w = pow(a.theta, -2.0 * (double)j / (double)a.D);
+    const double w = exp2(-2.0 * (double)j / (double)a.D * a.log2_theta);  // theta^(-2j/D)
     double sn, cn;
     sincos((double)pos * w, &sn, &cn);
     a.rope_cs[(size_t)t * (a.D / 2) + j] = make_float2((float)cn, (float)sn);
@@ -848,7 +850,7 @@ extern "C" int32_t segkv_qkv_rope_append(const segkv_dims* dims, const segkv_met
   ra.Hkv = Hkv;
   ra.D = D;
   ra.pool_pages = pool_pages;
-  ra.theta = rope_theta;
+  ra.log2_theta = std::log2(rope_theta);
   qkv_rows_kernel<<<(unsigned)T, kRowThreads, 0, s>>>(ra);
   SEGKV_LAUNCH_CHECK();
   QkvArgs a;
